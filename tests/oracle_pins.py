@@ -1,0 +1,352 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each pin_* function takes the oracle module and raises AssertionError when the
+oracle disagrees with what the pages, the mathematics or an independent library
+routine fix.  They are plain functions so that the mutation test can run them
+against an oracle with a planted mistake.
+"""
+
+import numpy as np
+import torch
+
+import golden_io
+
+F32 = np.float32
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _h_blocks(x, block):
+    nb = -(-x.size // block)
+    pad = np.zeros(nb * block, x.dtype)
+    pad[: x.size] = x
+    return pad.reshape(nb, block)
+
+
+# -- P-1: error feedback with e = 0 and an identity compressor reproduces g -------------------
+
+def pin_identity_compressor(O):
+    rng = _rng(1)
+    n = 1000
+    e = np.zeros(n, F32)
+    for _ in range(5):
+        g = (rng.standard_normal(n) * 1e-3).astype(F32)
+        out = O.compensate_quantize(g, e, bits=4, block=128, beta=0.9,
+                                    compressor=lambda h: (h.copy(), {}))
+        assert np.array_equal(out["d"].view(np.uint32), g.view(np.uint32)), "transmitted != g"
+        assert not np.any(out["e_new"]), "error left non-zero"
+        e = out["e_new"]
+
+
+# -- P-2: beta = 0 is plain error feedback, e' = h - d bitwise (Eqn. (4)) --------------------
+
+def pin_beta_zero_is_efc(O):
+    rng = _rng(2)
+    n = 3000
+    g = (rng.standard_normal(n) * 1e-3).astype(F32)
+    e = (rng.standard_normal(n) * 1e-4).astype(F32)
+    out = O.compensate_quantize(g, e, bits=4, block=128, beta=0.0)
+    h = g + e
+    assert np.array_equal(out["e_new"], h - out["d"])
+
+
+# -- P-3: per-element quantisation error bound step/2 -------------------------------------------
+
+def pin_quantisation_bound(O):
+    rng = _rng(3)
+    for bits, block in ((4, 128), (8, 256), (4, 64), (2, 128)):
+        n = 5 * block + 37
+        g = (rng.standard_t(3, n) * 1e-3).astype(F32)
+        e = (rng.standard_normal(n) * 1e-4).astype(F32)
+        out = O.compensate_quantize(g, e, bits=bits, block=block, beta=0.5)
+        h = g + e
+        hb = _h_blocks(h, block)
+        absmax = np.abs(hb).max(axis=1)
+        assert np.array_equal(out["absmax"], absmax), "absmax is not the block max |h|"
+        qmax = (1 << (bits - 1)) - 1
+        q = out["q"]
+        assert q.min() >= -qmax - 1 and q.max() <= qmax
+        step = (absmax.astype(np.float64) / qmax)
+        bound = np.repeat(step, block)[:n] * (0.5 + 4 * qmax * 2.0 ** -24)
+        r = np.abs(h.astype(np.float64) - out["d"].astype(np.float64))
+        assert np.all(r <= bound), "|h - d| exceeds step/2"
+
+
+# -- P-4: the moving-average error stays bounded over a 1000-step random walk --------------------
+
+def pin_random_walk_bounded(O):
+    rng = _rng(4)
+    n, block, beta = 2048, 128, 0.9
+    g = (rng.standard_normal(n) * 1e-3).astype(F32)
+    e = np.zeros(n, F32)
+    run_bound = np.zeros(n)
+    worst = 0.0
+    for _ in range(1000):
+        g = (g + rng.standard_normal(n) * 1e-4).astype(F32)
+        out = O.compensate_quantize(g, e, bits=4, block=block, beta=beta)
+        h = g + e
+        step = np.abs(_h_blocks(h, block)).max(axis=1).astype(np.float64) / 7
+        run_bound = np.maximum(run_bound, np.repeat(step, block)[:n] / 2)
+        e = out["e_new"]
+        ratio = np.abs(e.astype(np.float64)) / np.maximum(run_bound, 1e-30)
+        worst = max(worst, float(ratio.max()))
+    assert worst <= 1 + 1e-5, f"|e| exceeded the running max of step/2 (ratio {worst})"
+
+
+# -- P-5: telescoping identity of Eqn. (5), the non-accumulation of Eqn. (6) ----------------------
+
+def pin_telescoping(O):
+    """sum_i (g_i - d_i) = (e_K - e_0) / (1 - beta) in real arithmetic (float64 twin)."""
+    rng = _rng(5)
+    n, beta, K = 4096, 0.9, 50
+    e = np.zeros(n, np.float64)
+    e0 = e.copy()
+    acc = np.zeros(n, np.float64)
+    gabs = 0.0
+    for _ in range(K):
+        g = (rng.standard_t(3, n) * 1e-3).astype(F32).astype(np.float64)
+        out = O.compensate_quantize(g, e, bits=4, block=128, beta=beta,
+                                    grad_dtype="f64", err_dtype="f64", ftype=np.float64)
+        acc += g - out["d"]
+        gabs += np.abs(g).max()
+        e = out["e_new"]
+    rhs = (e - e0) / (1 - beta)
+    assert np.max(np.abs(acc - rhs)) <= 1e-11 * gabs, "error accumulates: telescoping broken"
+    # and in float32 the same chain stays within the accumulated rounding
+    rng = _rng(5)
+    e = np.zeros(n, F32)
+    acc = np.zeros(n, np.float64)
+    for _ in range(K):
+        g = (rng.standard_t(3, n) * 1e-3).astype(F32)
+        out = O.compensate_quantize(g, e, bits=4, block=128, beta=beta)
+        acc += g.astype(np.float64) - out["d"].astype(np.float64)
+        e = out["e_new"]
+    rhs = e.astype(np.float64) / (1 - beta)
+    assert np.max(np.abs(acc - rhs)) <= 1e-5 * gabs
+
+
+# -- P-6: the fixed-scale compressor of Eqn. (1) on hand-worked values ----------------------------
+
+def pin_fixed_scale_golden(O):
+    s = 2.0 ** 19
+    for bits, m, expect in golden_io.rounding_cases():
+        h = np.array([m * 2.0 ** -19], F32)
+        q, step = O.fixed_scale_quantize(h, bits, s)
+        assert int(q[0]) == expect, f"Round_{bits}({m}) -> {int(q[0])}, want {expect}"
+        assert step == F32(2.0 ** -19)
+
+
+# -- P-7: PyTorch's own quantiser (the page names it as the one used) ------------------------------
+
+def pin_torch_quantiser(O):
+    rng = _rng(7)
+    block = 256
+    nb = 80
+    n = nb * block
+    h = (rng.standard_t(3, n) * 1e-3).astype(F32)
+    # half of the blocks sit one ulp off the rounding boundaries (k + 1/2) * step, where
+    # multiplying by fl(1/step) and dividing by step give different codes
+    for b in range(nb // 2, nb):
+        a = F32(rng.uniform(1e-4, 1e-2))
+        step = a / F32(127)
+        k = rng.integers(-126, 126, block - 1).astype(F32)
+        v = ((k + F32(0.5)) * step).astype(F32)
+        v = np.nextafter(v, np.where(rng.random(block - 1) < 0.5, -np.inf, np.inf).astype(F32))
+        h[b * block] = a
+        h[b * block + 1:(b + 1) * block] = v
+    # 8 bits against torch.quantize_per_channel(qint8) with one scale per block
+    out = O.compensate_quantize(h, np.zeros(n, F32), bits=8, block=block, beta=0.9)
+    step = O.block_steps(out["absmax"], 8)
+    tq = torch.quantize_per_channel(torch.from_numpy(h.reshape(nb, block)),
+                                    torch.from_numpy(step.astype(np.float64)),
+                                    torch.zeros(nb, dtype=torch.int64), 0, torch.qint8)
+    assert np.array_equal(tq.int_repr().numpy().reshape(-1).astype(np.int64), out["q"])
+    # 4 bits, one block at a time, against quint4x2 (offset-8 nibbles, element 2j low)
+    out4 = O.compensate_quantize(h, np.zeros(n, F32), bits=4, block=block, beta=0.9)
+    step4 = O.block_steps(out4["absmax"], 4)
+    for b in range(nb):
+        t = torch.quantize_per_tensor(torch.from_numpy(h[b * block:(b + 1) * block]),
+                                      float(step4[b]), 8, torch.quint4x2)
+        ours = out4["codes"][b * block // 2:(b + 1) * block // 2]
+        assert np.array_equal(t.int_repr().numpy() ^ 0x88, ours), f"4-bit block {b} differs"
+
+
+# -- P-8: Top-k by brute force on tiny inputs with many ties --------------------------------------
+
+def _brute_topk(key, k):
+    n = key.size
+    sel = []
+    for i in range(n):
+        better = sum(1 for j in range(n) if key[j] > key[i] or (key[j] == key[i] and j < i))
+        if better < k:
+            sel.append(i)
+    return np.array(sel, dtype=np.int64)
+
+
+def pin_topk_brute_force(O):
+    rng = _rng(8)
+    for trial in range(200):
+        n = int(rng.integers(1, 65))
+        k = int(rng.integers(1, n + 1))
+        key = rng.integers(0, 6, n).astype(np.uint32)  # few distinct values: many ties
+        got = O.topk_order_select(key, k)
+        assert np.array_equal(got, _brute_topk(key, k)), (n, k, key)
+    for trial in range(30):
+        chunk = int(rng.choice([4, 8, 16]))
+        n = int(rng.integers(1, 4 * chunk))
+        k = int(rng.integers(1, chunk + 1))
+        g = rng.choice(np.array([0, 0.5, -0.5, 1, -1, 2], F32), n).astype(F32)
+        out = O.topk_quantize(g, np.zeros(n, F32), chunk=chunk, k=k)
+        for c in range(-(-n // chunk)):
+            hc = g[c * chunk:(c + 1) * chunk]
+            keff = min(k, hc.size)
+            want = _brute_topk(np.abs(hc).view(np.uint32), keff)
+            idx = out["idx"][c * k:(c + 1) * k]
+            assert np.array_equal(idx[:keff].astype(np.int64), want)
+            assert np.all(idx[keff:] == 0xFFFF)
+            mask = np.zeros(hc.size, bool)
+            mask[want] = True
+            assert np.array_equal(out["e_new"][c * chunk:c * chunk + hc.size][~mask], hc[~mask])
+
+
+# -- P-9: payload byte layout and round trip --------------------------------------------------------
+
+def pin_pack_layout(O):
+    for bits, codes, want in golden_io.pack_cases():
+        got = O.pack_codes(np.array(codes), bits)
+        assert bytes(got.tobytes()) == want, (bits, codes, got.tobytes().hex(), want.hex())
+        back = O.unpack_codes(got, bits, len(codes))
+        assert list(back) == codes
+    rng = _rng(9)
+    for bits in (2, 4, 8):
+        for n in (1, 2, 3, 7, 64, 1001):
+            q = rng.integers(-(1 << (bits - 1)), 1 << (bits - 1), n)
+            assert np.array_equal(O.unpack_codes(O.pack_codes(q, bits), bits, n), q)
+
+
+# -- hand-worked compensate-quantize, dequant-reduce and Top-k steps ---------------------------
+
+def pin_cq_worked(O):
+    for c in golden_io.cq_cases():
+        out = O.compensate_quantize(c["g"], c["e"], bits=c["bits"], block=c["block"], beta=c["beta"])
+        assert np.array_equal(out["absmax"], c["absmax"]), ("absmax", out["absmax"], c["absmax"])
+        assert out["codes"].tobytes() == c["codes"], ("codes", out["codes"].tobytes().hex())
+        assert np.array_equal(out["e_new"], c["e_new"]), ("e_new", out["e_new"], c["e_new"])
+
+
+def pin_dr_worked(O):
+    c = golden_io.dr_case()
+    out = O.dequant_reduce(c["peers"], c["n"], bits=c["bits"], block=c["block"],
+                           out_scale=c["out_scale"])
+    assert np.array_equal(out, c["out"]), (out, c["out"])
+
+
+def pin_topk_worked(O):
+    for c in golden_io.topk_cases():
+        out = O.topk_quantize(c["g"], c["e"], chunk=c["chunk"], k=c["k"], decay=c["decay"])
+        assert np.array_equal(out["idx"], c["idx"]), ("idx", out["idx"], c["idx"])
+        assert out["codes"].tobytes() == c["codes"], ("codes", out["codes"].tobytes().hex())
+        assert np.array_equal(out["absmax"], c["absmax"])
+        assert np.array_equal(out["e_new"], c["e_new"]), ("e_new", out["e_new"], c["e_new"])
+
+
+# -- P-10: dequant-reduce special cases and the high-precision average -----------------------------
+
+def pin_dequant_reduce(O):
+    rng = _rng(10)
+    n, block = 3 * 256 + 100, 256
+    outs = []
+    for p in range(5):
+        g = (rng.standard_t(3, n) * 1e-3).astype(F32)
+        outs.append(O.compensate_quantize(g, np.zeros(n, F32), bits=4, block=block, beta=0.9))
+    pay = [(o["codes"], o["absmax"]) for o in outs]
+    # one peer, scale 1: exactly that peer's decompressed value
+    one = O.dequant_reduce(pay[:1], n, bits=4, block=block, out_scale=1.0)
+    assert np.array_equal(one, outs[0]["d"])
+    # two identical peers averaged: exact
+    two = O.dequant_reduce([pay[1], pay[1]], n, bits=4, block=block, out_scale=0.5)
+    assert np.array_equal(two, outs[1]["d"])
+    # five peers: the float64 average of the decompressed values, within fp32 rounding
+    got = O.dequant_reduce(pay, n, bits=4, block=block, out_scale=F32(1) / F32(5))
+    ds = np.stack([o["d"].astype(np.float64) for o in outs])
+    want = ds.sum(0) / 5
+    bound = 2.0 ** -23 * (len(outs) + 1) * np.abs(ds).sum(0) / 5 + 1e-45
+    assert np.all(np.abs(got.astype(np.float64) - want) <= bound)
+    # bf16 output is the RNE of the fp32 output
+    gotb = O.dequant_reduce(pay, n, bits=4, block=block, out_scale=F32(1) / F32(5), out_dtype="bf16")
+    tb = torch.from_numpy(got).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gotb, tb)
+
+
+# -- P-11: all-zero blocks ---------------------------------------------------------------------
+
+def pin_zero_blocks(O):
+    rng = _rng(11)
+    block = 128
+    g = (rng.standard_normal(6 * block) * 1e-3).astype(F32)
+    g[block:3 * block] = 0
+    g[5 * block:] = 0
+    e = np.zeros_like(g)
+    for _ in range(3):
+        out = O.compensate_quantize(g, e, bits=4, block=block, beta=0.9)
+        for b in (1, 2, 5):
+            assert out["absmax"][b] == 0
+            assert not np.any(out["q"][b * block:(b + 1) * block])
+            assert not np.any(out["e_new"][b * block:(b + 1) * block])
+        e = out["e_new"]
+
+
+# -- P-12: bf16 rounding equals torch's conversion ---------------------------------------------
+
+def pin_bf16_rne(O):
+    rng = _rng(12)
+    x = (rng.standard_normal(100000) * rng.choice([1e-6, 1e-3, 1.0, 1e3], 100000)).astype(F32)
+    u = x.view(np.uint32).copy()
+    u[:2000] = (u[:2000] & 0xFFFF0000) | 0x8000  # exact ties, both parities of the kept bit
+    u[2000:4000] = (u[2000:4000] & 0xFFFF0000) | 0x7FFF
+    u[4000:6000] = (u[4000:6000] & 0xFFFF0000) | 0x8001
+    x = u.view(F32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_rne(x), want)
+    assert np.array_equal(O.bf16_to_f32(want), torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+# -- SparseLoCo error feedback: transmitted + final error telescopes to the gradient sum ------------
+
+def pin_topk_error_feedback(O):
+    """decay = 1: sum_k transmitted_k = sum_k g_k - e_K (float64 twin, exact up to rounding)."""
+    rng = _rng(13)
+    n, chunk, k, K = 4 * 256 + 50, 256, 6, 20
+    e = np.zeros(n)
+    sent = np.zeros(n)
+    gsum = np.zeros(n)
+    for _ in range(K):
+        g = (rng.standard_normal(n) * 1e-3).astype(F32).astype(np.float64)
+        out = O.topk_quantize(g, e, chunk=chunk, k=k, decay=1.0, ftype=np.float64)
+        sent += out["h"] - out["e_new"]
+        gsum += g
+        e = out["e_new"]
+        # kept values carry at most half a step of error; the rest are untouched
+        for c in range(-(-n // chunk)):
+            lo = c * chunk
+            hc = out["h"][lo:lo + chunk]
+            idx = out["idx"][c * k:(c + 1) * k]
+            idx = idx[idx != 0xFFFF].astype(np.int64)
+            am = out["absmax"][c]
+            assert am == np.abs(hc).max()
+            assert np.all(np.abs(out["e_new"][lo + idx]) <= am / 2 * (1 + 1e-12))
+            # exactly k entries move: the others equal h
+            mask = np.ones(hc.size, bool)
+            mask[idx] = False
+            assert np.array_equal(out["e_new"][lo:lo + chunk][mask], hc[mask])
+    assert np.max(np.abs(sent - (gsum - e))) <= 1e-12 * K
+
+
+ALL_PINS = [
+    pin_identity_compressor, pin_beta_zero_is_efc, pin_quantisation_bound,
+    pin_random_walk_bounded, pin_telescoping, pin_fixed_scale_golden, pin_torch_quantiser,
+    pin_topk_brute_force, pin_pack_layout, pin_cq_worked, pin_dr_worked, pin_topk_worked,
+    pin_dequant_reduce, pin_zero_blocks, pin_bf16_rne, pin_topk_error_feedback,
+]

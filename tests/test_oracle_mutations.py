@@ -1,0 +1,137 @@
+"""Plant plausible mistakes in the CPU oracle and check that some pin catches each.
+
+This shows the pins are strong enough: a dropped term, a wrong sign, a swapped
+weight, an off-by-one block, the wrong rounding or tie rule, a swapped nibble order
+or a missing sign extension must each fail at least one pin.  Mistakes are planted
+only in the oracle, on the CPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+
+O = oracle.loco_oracle
+_orig = {name: getattr(O, name) for name in dir(O) if not name.startswith("__")}
+
+
+def _drop_beta_term(e, r, beta):
+    ft = e.dtype.type
+    return (ft(1) - ft(beta)) * r
+
+
+def _swap_weights(e, r, beta):
+    ft = e.dtype.type
+    return (ft(1) - ft(beta)) * e + ft(beta) * r
+
+
+def _compensate_minus(g, e):
+    return g - e
+
+
+def _floor_quantise(h, bits, block):
+    q, absmax, step = _orig["absmax_quantize"](h, bits, block)
+    hb, nb = _orig["_blocks"](h, block)
+    inv = np.zeros(nb, h.dtype)
+    np.divide(h.dtype.type(1), step, out=inv, where=step != 0)
+    qmax = (1 << (bits - 1)) - 1
+    qf = np.clip(np.floor(hb * inv[:, None]), -qmax - 1, qmax).astype(np.int64)
+    return qf.reshape(-1)[: h.size], absmax, step
+
+
+def _half_away_quantise(h, bits, block):
+    q, absmax, step = _orig["absmax_quantize"](h, bits, block)
+    hb, nb = _orig["_blocks"](h, block)
+    inv = np.zeros(nb, h.dtype)
+    np.divide(h.dtype.type(1), step, out=inv, where=step != 0)
+    x = hb * inv[:, None]
+    qmax = (1 << (bits - 1)) - 1
+    qa = np.clip(np.sign(x) * np.floor(np.abs(x) + h.dtype.type(0.5)), -qmax - 1, qmax)
+    return qa.astype(np.int64).reshape(-1)[: h.size], absmax, step
+
+
+def _shifted_block(h, bits, block):
+    q, absmax, step = _orig["absmax_quantize"](np.roll(h, 1), bits, block)
+    return np.roll(q, -1), absmax, step
+
+
+def _divide_not_reciprocal(h, bits, block):
+    hb, nb = _orig["_blocks"](h, block)
+    qmax = (1 << (bits - 1)) - 1
+    absmax = np.max(np.abs(hb), axis=1)
+    step = np.zeros(nb, h.dtype)
+    np.divide(absmax, h.dtype.type(qmax), out=step, where=absmax != 0)
+    x = np.zeros_like(hb)
+    np.divide(hb, step[:, None], out=x, where=step[:, None] != 0)
+    q = np.clip(np.rint(x), -qmax - 1, qmax).astype(np.int64)
+    return q.reshape(-1)[: h.size], absmax, step
+
+
+def _dequantize_no_step(q, step):
+    return q.astype(step.dtype)
+
+
+def _dequantize_neg(q, step):
+    return -(q.astype(step.dtype) * step)
+
+
+def _ties_high(key, k):
+    key = np.asarray(key)
+    neg = -(key.astype(np.int64)) if key.dtype.kind in "ui" else -key
+    order = np.argsort(neg[::-1], kind="stable")
+    return np.sort((key.size - 1 - order)[:k])
+
+
+def _pack_swapped(q, bits):
+    p = _orig["pack_codes"](q, bits)
+    if bits == 4:
+        return ((p >> 4) | (p << 4)).astype(np.uint8)
+    return p
+
+
+def _unpack_unsigned(packed, bits, n):
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    per = 8 // bits
+    mask = (1 << bits) - 1
+    return np.stack([(p >> (bits * t)) & mask for t in range(per)], axis=1).reshape(-1)[:n]
+
+
+def _bf16_truncate(x):
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _steps_no_qmax(absmax, bits):
+    return np.asarray(absmax).copy()
+
+
+MUTATIONS = {
+    "error_update drops beta*e": ("error_update", _drop_beta_term),
+    "error_update swaps beta and 1-beta": ("error_update", _swap_weights),
+    "compensate subtracts e": ("compensate", _compensate_minus),
+    "floor instead of rint": ("absmax_quantize", _floor_quantise),
+    "ties away from zero": ("absmax_quantize", _half_away_quantise),
+    "scale of the wrong block": ("absmax_quantize", _shifted_block),
+    "divide instead of reciprocal-multiply": ("absmax_quantize", _divide_not_reciprocal),
+    "decompressor drops step": ("dequantize", _dequantize_no_step),
+    "decompressor sign": ("dequantize", _dequantize_neg),
+    "top-k ties to the higher index": ("topk_order_select", _ties_high),
+    "nibbles swapped": ("pack_codes", _pack_swapped),
+    "no sign extension": ("unpack_codes", _unpack_unsigned),
+    "bf16 truncation": ("bf16_rne", _bf16_truncate),
+    "decoder step without /qmax": ("block_steps", _steps_no_qmax),
+}
+
+
+@pytest.mark.parametrize("label", sorted(MUTATIONS))
+def test_mutation_is_caught(label, monkeypatch):
+    name, bad = MUTATIONS[label]
+    monkeypatch.setattr(O, name, bad)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(O)
+        except AssertionError:
+            caught.append(pin.__name__)
+        except Exception as ex:  # a crash inside a pin also counts as a failed pin
+            caught.append(f"{pin.__name__}:{type(ex).__name__}")
+    assert caught, f"no pin catches: {label}"
