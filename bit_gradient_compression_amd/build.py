@@ -1,0 +1,72 @@
+"""Build libloco.so (gfx950) in-tree with hipcc.
+
+Every translation unit is compiled in parallel, then linked.  Flags that fix the
+arithmetic: no fused multiply-add contraction, no fast math, IEEE division and denormals
+kept, and no packed-fp32 instructions.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB_NAME = "libloco.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = ["abi.hip", "cq.hip", "dr.hip", "tk.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def compile_flags(extra=()):
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+            "-ffp-contract=off", "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
+            "-fno-gpu-flush-denormals-to-zero",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            f"-I{INCLUDE}", f"-I{CSRC}", *extra]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r
+
+
+def build(out_path: str = LIB_PATH, extra_flags=(), jobs: int | None = None, verbose=False) -> str:
+    """Compile and link the library; returns the path of the .so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    flags = compile_flags(extra_flags)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))
+    with ThreadPoolExecutor(jobs) as ex:
+        for r in ex.map(_run, cmds):
+            if verbose and r.stderr:
+                print(r.stderr, file=sys.stderr)
+    tmp = out_path + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, out_path)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

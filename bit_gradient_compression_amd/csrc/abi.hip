@@ -1,0 +1,214 @@
+// C ABI of the library: argument validation on the host, then one launch per call on
+// the caller's stream.  Validation runs before any HIP call, so an error status means
+// nothing was launched and nothing was written.
+
+#include <math.h>
+#include <string.h>
+
+#include "loco.h"
+#include "loco_internal.hpp"
+
+#define LOCO_API extern "C" __attribute__((visibility("default")))
+
+namespace loco {
+
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64) cache[dev] = cus;
+    return cus;
+}
+
+namespace {
+
+// Workgroups per compute unit of the persistent streaming grids.
+constexpr int kWgPerCu = 8;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool bits_ok(int bits) { return bits == 2 || bits == 4 || bits == 8; }
+bool block_ok(int block) { return block == 64 || block == 128 || block == 256 || block == 512; }
+bool dtype_ok(int d) { return d == LOCO_F32 || d == LOCO_BF16; }
+int dtype_size(int d) { return d == LOCO_BF16 ? 2 : 4; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, int64_t bytes) { return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+int64_t code_bytes(int64_t n, int bits) { return (n * bits + 7) / 8; }
+int64_t nblocks(int64_t n, int block) { return (n + block - 1) / block; }
+
+// Sizes beyond this are refused: far above any device memory, and safe from overflow in
+// the byte arithmetic above.
+constexpr int64_t kMaxElems = (int64_t)1 << 52;
+
+}  // namespace
+}  // namespace loco
+
+using namespace loco;
+
+LOCO_API int loco_version(void) { return 10000; }
+
+LOCO_API const char* loco_status_string(int status) {
+    switch (status) {
+        case LOCO_OK: return "LOCO_OK";
+        case LOCO_ERR_INVALID: return "LOCO_ERR_INVALID: invalid argument";
+        case LOCO_ERR_ALIGN: return "LOCO_ERR_ALIGN: device pointer not 16-byte aligned";
+        case LOCO_ERR_UNSUPPORTED: return "LOCO_ERR_UNSUPPORTED: valid but not built";
+        case LOCO_ERR_HIP: return "LOCO_ERR_HIP: kernel launch failed";
+    }
+    return "unknown status";
+}
+
+LOCO_API int loco_compensate_quantize(const loco_cq_segment_t* segs, int nseg,
+                                      loco_dtype_t grad_dtype, loco_dtype_t err_dtype,
+                                      int bits, int block, float beta, float fixed_scale,
+                                      void* stream) {
+    if (nseg < 0 || (nseg > 0 && !segs)) return LOCO_ERR_INVALID;
+    if (!dtype_ok(grad_dtype) || !dtype_ok(err_dtype)) return LOCO_ERR_INVALID;
+    if (bits < 1 || bits > 8) return LOCO_ERR_INVALID;
+    if (!bits_ok(bits)) return LOCO_ERR_UNSUPPORTED;
+    if (!isfinite(beta) || beta < 0.0f || beta > 1.0f) return LOCO_ERR_INVALID;
+    if (!isfinite(fixed_scale) || fixed_scale < 0.0f) return LOCO_ERR_INVALID;
+    const bool fixed = fixed_scale > 0.0f;
+    if (!fixed) {
+        if (block <= 0) return LOCO_ERR_INVALID;
+        if (!block_ok(block)) return LOCO_ERR_UNSUPPORTED;
+    }
+    const int gs = dtype_size(grad_dtype), es = dtype_size(err_dtype);
+    int64_t live = 0;
+    for (int i = 0; i < nseg; ++i) {
+        const loco_cq_segment_t& s = segs[i];
+        if (s.n < 0 || s.n > kMaxElems) return LOCO_ERR_INVALID;
+        if (s.n == 0) continue;
+        if (!s.grad || !s.err || !s.codes || (!fixed && !s.absmax)) return LOCO_ERR_INVALID;
+        if (!aligned16(s.grad) || !aligned16(s.err) || !aligned16(s.codes) || (!fixed && !aligned16(s.absmax)))
+            return LOCO_ERR_ALIGN;
+        Range r[4] = {range_of(s.grad, s.n * gs), range_of(s.err, s.n * es),
+                      range_of(s.codes, code_bytes(s.n, bits)),
+                      range_of(s.absmax, fixed ? 0 : nblocks(s.n, block) * 4)};
+        for (int a = 0; a < 4; ++a)
+            for (int b = a + 1; b < 4; ++b)
+                if (overlap(r[a], r[b])) return LOCO_ERR_INVALID;
+        ++live;
+    }
+    if (live == 0) return LOCO_OK;
+
+    CqParams p;
+    memset(&p, 0, sizeof(p));
+    p.beta = beta;
+    p.omega = 1.0f - beta;
+    if (fixed) {
+        p.fixed_inv = fixed_scale;
+        p.fixed_step = 1.0f / fixed_scale;
+    }
+    const int max_blocks = device_cus() * kWgPerCu;
+    hipStream_t st = (hipStream_t)stream;
+    int i = 0;
+    while (i < nseg) {
+        p.nseg = 0;
+        p.ntiles = 0;
+        for (; i < nseg && p.nseg < kCqMaxSeg; ++i) {
+            const loco_cq_segment_t& s = segs[i];
+            if (s.n == 0) continue;
+            CqSegDev& d = p.seg[p.nseg++];
+            d.g = s.grad;
+            d.e = s.err;
+            d.codes = s.codes;
+            d.absmax = s.absmax;
+            d.n = s.n;
+            d.tile0 = p.ntiles;
+            p.ntiles += (s.n + kCqTile - 1) / kCqTile;
+        }
+        if (p.nseg == 0) break;
+        if (launch_cq(p, grad_dtype == LOCO_BF16, err_dtype == LOCO_BF16, bits, block, fixed, max_blocks, st) !=
+            hipSuccess)
+            return LOCO_ERR_HIP;
+    }
+    return LOCO_OK;
+}
+
+LOCO_API int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_t n, int bits,
+                                 int block, float fixed_scale, float out_scale, void* out,
+                                 loco_dtype_t out_dtype, void* stream) {
+    if (n < 0 || n > kMaxElems) return LOCO_ERR_INVALID;
+    if (npeers < 1 || !peers) return LOCO_ERR_INVALID;
+    if (npeers > kDrMaxPeers) return LOCO_ERR_UNSUPPORTED;
+    if (bits < 1 || bits > 8) return LOCO_ERR_INVALID;
+    if (!bits_ok(bits)) return LOCO_ERR_UNSUPPORTED;
+    if (!isfinite(fixed_scale) || fixed_scale < 0.0f) return LOCO_ERR_INVALID;
+    if (!isfinite(out_scale)) return LOCO_ERR_INVALID;
+    if (!dtype_ok(out_dtype)) return LOCO_ERR_INVALID;
+    const bool fixed = fixed_scale > 0.0f;
+    if (!fixed) {
+        if (block <= 0) return LOCO_ERR_INVALID;
+        if (!block_ok(block)) return LOCO_ERR_UNSUPPORTED;
+    }
+    if (n == 0) return LOCO_OK;
+    if (!out) return LOCO_ERR_INVALID;
+    if (!aligned16(out)) return LOCO_ERR_ALIGN;
+    const Range ro = range_of(out, n * dtype_size(out_dtype));
+    for (int i = 0; i < npeers; ++i) {
+        if (!peers[i].codes || (!fixed && !peers[i].absmax)) return LOCO_ERR_INVALID;
+        if (!aligned16(peers[i].codes) || (!fixed && !aligned16(peers[i].absmax))) return LOCO_ERR_ALIGN;
+        if (overlap(ro, range_of(peers[i].codes, code_bytes(n, bits)))) return LOCO_ERR_INVALID;
+        if (!fixed && overlap(ro, range_of(peers[i].absmax, nblocks(n, block) * 4))) return LOCO_ERR_INVALID;
+    }
+    DrParams p;
+    memset(&p, 0, sizeof(p));
+    for (int i = 0; i < npeers; ++i) {
+        p.peer[i].codes = peers[i].codes;
+        p.peer[i].absmax = peers[i].absmax;
+    }
+    p.npeers = npeers;
+    p.n = n;
+    p.ntiles = (n + kDrTile - 1) / kDrTile;
+    p.fixed_step = fixed ? 1.0f / fixed_scale : 0.0f;
+    p.out_scale = out_scale;
+    p.out = out;
+    if (launch_dr(p, bits, block, fixed, out_dtype == LOCO_BF16, device_cus() * kWgPerCu, (hipStream_t)stream) !=
+        hipSuccess)
+        return LOCO_ERR_HIP;
+    return LOCO_OK;
+}
+
+LOCO_API int loco_topk_quantize(const float* grad, float* err, int64_t n, int chunk, int k, int bits,
+                                float ef_decay, uint16_t* idx, uint8_t* codes, float* absmax,
+                                void* stream) {
+    if (n < 0 || n > kMaxElems) return LOCO_ERR_INVALID;
+    if (chunk <= 0 || chunk > 65536) return LOCO_ERR_INVALID;
+    if (k < 1 || k > chunk) return LOCO_ERR_INVALID;
+    if (bits < 1 || bits > 8) return LOCO_ERR_INVALID;
+    if (!isfinite(ef_decay) || ef_decay < 0.0f || ef_decay > 1.0f) return LOCO_ERR_INVALID;
+    if (!bits_ok(bits)) return LOCO_ERR_UNSUPPORTED;
+    if (chunk != 256 && chunk != 512 && chunk != 1024 && chunk != 2048 && chunk != 4096)
+        return LOCO_ERR_UNSUPPORTED;
+    if (n == 0) return LOCO_OK;
+    if (!grad || !err || !idx || !codes || !absmax) return LOCO_ERR_INVALID;
+    if (!aligned16(grad) || !aligned16(err) || !aligned16(idx) || !aligned16(codes) || !aligned16(absmax))
+        return LOCO_ERR_ALIGN;
+    const int64_t chunks = (n + chunk - 1) / chunk;
+    Range r[5] = {range_of(grad, n * 4), range_of(err, n * 4), range_of(idx, chunks * k * 2),
+                  range_of(codes, chunks * code_bytes(k, bits)), range_of(absmax, chunks * 4)};
+    for (int a = 0; a < 5; ++a)
+        for (int b = a + 1; b < 5; ++b)
+            if (overlap(r[a], r[b])) return LOCO_ERR_INVALID;
+    TkParams p;
+    p.g = grad;
+    p.e = err;
+    p.n = n;
+    p.k = k;
+    p.decay = ef_decay;
+    p.idx = idx;
+    p.codes = codes;
+    p.absmax = absmax;
+    if (launch_tk(p, chunk, bits, (hipStream_t)stream) != hipSuccess) return LOCO_ERR_HIP;
+    return LOCO_OK;
+}

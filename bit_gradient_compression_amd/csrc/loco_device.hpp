@@ -1,0 +1,83 @@
+// Device helpers for the gfx950 kernels: vector types, bf16 conversion, wavefront
+// reductions and ballots.  Every kernel of the library includes this file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace loco {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---- bf16 ---------------------------------------------------------------------
+
+// bf16 -> f32 is exact: the pattern becomes the high half of the f32 pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// f32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+    __bf16 a = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, a);
+}
+
+// ---- wavefront primitives -------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Number of set bits of m in the lanes below this one.
+__device__ __forceinline__ int mbcnt(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Max of v over aligned groups of LANES consecutive lanes (LANES a power of two up
+// to 64); every lane of the group gets the result.  All 64 lanes must be active.
+// Unsigned compare: applied to the bit patterns of non-negative floats it is the
+// float max, exactly.
+template <int LANES>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+    if constexpr (LANES >= 2) v = max(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+    if constexpr (LANES >= 4) v = max(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+    if constexpr (LANES >= 8) v = max(v, dpp<0x141>(v));   // row_half_mirror
+    if constexpr (LANES >= 16) v = max(v, dpp<0x140>(v));  // row_mirror
+    if constexpr (LANES >= 32) {
+        auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = max((uint32_t)s[0], (uint32_t)s[1]);
+    }
+    if constexpr (LANES >= 64) {
+        auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = max((uint32_t)s[0], (uint32_t)s[1]);
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return group_max_u32<64>(v); }
+
+// Position of the r-th (1-based) set bit of m (r >= 1).  If m holds fewer than r set
+// bits the result is still a lane number (0..63), never out of range.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
+    for (int t = 1; t < r; ++t) m &= m - 1;
+    return m ? __builtin_ctzll(m) : 63;
+}
+
+// Wave-uniform value as an SGPR.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace loco

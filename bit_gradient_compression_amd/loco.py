@@ -1,0 +1,173 @@
+"""Python binding of libloco.so (ctypes): argument marshalling only.
+
+Every function takes torch tensors (device memory) and passes their pointers, sizes and
+the current HIP stream to the C ABI of the same name; every step of the computation
+runs in the library's HIP kernels.  There is no fallback: if the library is missing or
+a call returns an error status, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+LOCO_F32 = 0
+LOCO_BF16 = 1
+LOCO_OK = 0
+LOCO_ERR_INVALID = -1
+LOCO_ERR_ALIGN = -2
+LOCO_ERR_UNSUPPORTED = -3
+LOCO_ERR_HIP = -4
+LOCO_MAX_PEERS = 128
+
+SYMBOLS = ["loco_compensate_quantize", "loco_dequant_reduce", "loco_topk_quantize",
+           "loco_status_string", "loco_version"]
+
+
+class LocoError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+
+
+class CqSegment(ctypes.Structure):
+    _fields_ = [("grad", ctypes.c_void_p), ("err", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("absmax", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+class Payload(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def load(path: str | None = None):
+    """Load libloco.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.loco_compensate_quantize.argtypes = [ctypes.POINTER(CqSegment), ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                             ctypes.c_float, ctypes.c_void_p]
+    lib.loco_compensate_quantize.restype = ctypes.c_int
+    lib.loco_dequant_reduce.argtypes = [ctypes.POINTER(Payload), ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+    lib.loco_dequant_reduce.restype = ctypes.c_int
+    lib.loco_topk_quantize.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.loco_topk_quantize.restype = ctypes.c_int
+    lib.loco_status_string.argtypes = [ctypes.c_int]
+    lib.loco_status_string.restype = ctypes.c_char_p
+    lib.loco_version.argtypes = []
+    lib.loco_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().loco_status_string(int(status)).decode()
+
+
+loco_status_string = status_string
+
+
+def _check(fn, status):
+    if status != LOCO_OK:
+        raise LocoError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LOCO_F32
+    if t.dtype == torch.bfloat16:
+        return LOCO_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def code_bytes(n: int, bits: int) -> int:
+    return (n * bits + 7) // 8
+
+
+def num_blocks(n: int, block: int) -> int:
+    return -(-n // block)
+
+
+def loco_compensate_quantize(segments, *, bits: int, block: int, beta: float, fixed_scale: float = 0.0,
+                             stream=None, grad_dtype=None, err_dtype=None) -> None:
+    """segments: iterable of (grad, err, codes, absmax) tensors; absmax may be None in
+    fixed-scale mode.  n of a segment is grad.numel()."""
+    segs = list(segments)
+    arr = (CqSegment * max(1, len(segs)))()
+    gd = ed = None
+    for i, (g, e, c, a) in enumerate(segs):
+        gd = _dtype_code(g) if gd is None else gd
+        ed = _dtype_code(e) if ed is None else ed
+        if _dtype_code(g) != gd or _dtype_code(e) != ed:
+            raise TypeError("all segments must share grad and err dtypes")
+        arr[i] = CqSegment(_ptr(g), _ptr(e), _ptr(c), _ptr(a), g.numel())
+    gd = gd if grad_dtype is None else grad_dtype
+    ed = ed if err_dtype is None else err_dtype
+    st = load().loco_compensate_quantize(arr, len(segs), LOCO_F32 if gd is None else gd,
+                                         LOCO_F32 if ed is None else ed, bits, block, beta,
+                                         fixed_scale, _stream(stream))
+    _check("loco_compensate_quantize", st)
+
+
+def loco_dequant_reduce(peers, n: int, *, bits: int, block: int, out, out_scale: float,
+                        fixed_scale: float = 0.0, stream=None) -> None:
+    """peers: iterable of (codes, absmax) tensors (absmax None in fixed-scale mode)."""
+    ps = list(peers)
+    arr = (Payload * max(1, len(ps)))()
+    for i, (c, a) in enumerate(ps):
+        arr[i] = Payload(_ptr(c), _ptr(a))
+    st = load().loco_dequant_reduce(arr if ps else None, len(ps), n, bits, block, fixed_scale, out_scale,
+                                    _ptr(out), _dtype_code(out), _stream(stream))
+    _check("loco_dequant_reduce", st)
+
+
+def loco_topk_quantize(grad, err, *, chunk: int, k: int, idx, codes, absmax, bits: int = 2,
+                       ef_decay: float = 1.0, stream=None) -> None:
+    if grad.dtype != torch.float32 or err.dtype != torch.float32:
+        raise TypeError("grad and err must be float32")
+    st = load().loco_topk_quantize(_ptr(grad), _ptr(err), grad.numel(), chunk, k, bits, ef_decay,
+                                   _ptr(idx), _ptr(codes), _ptr(absmax), _stream(stream))
+    _check("loco_topk_quantize", st)
+
+
+# short names
+compensate_quantize = loco_compensate_quantize
+dequant_reduce = loco_dequant_reduce
+topk_quantize = loco_topk_quantize

@@ -1,0 +1,172 @@
+"""The C ABI without a GPU: the library loads, exports every function include/loco.h
+declares, and refuses bad arguments on the host before any HIP call.
+
+Every call here either fails validation or has nothing to do (n == 0), so nothing is
+launched; the fake pointers are never dereferenced.
+"""
+import ctypes
+import glob
+import math
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+if torch.cuda.is_available():
+    # Fake pointers must never reach a real device: these checks run only where no GPU is.
+    pytest.skip("host-only validation tests (fake device pointers)", allow_module_level=True)
+
+from bit_gradient_compression_amd import build as B  # noqa: E402
+from bit_gradient_compression_amd import loco  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INV, ALIGN, UNSUP = loco.LOCO_OK, loco.LOCO_ERR_INVALID, loco.LOCO_ERR_ALIGN, loco.LOCO_ERR_UNSUPPORTED
+F32, BF16 = loco.LOCO_F32, loco.LOCO_BF16
+NAN = float("nan")
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(loco_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libloco.so is not built (run __graft_entry__.build())")
+    return loco.load()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for fn in ("loco_compensate_quantize", "loco_dequant_reduce", "loco_topk_quantize", "loco_status_string"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(loco_\w+)$", out, flags=re.M))
+    for fn in declared_functions():
+        assert fn in exported, fn
+        assert getattr(lib, fn) is not None
+    assert set(loco.SYMBOLS) == set(declared_functions())
+    # nothing else leaks out of the library with a loco_ prefix
+    assert exported == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for s in (OK, INV, ALIGN, UNSUP, loco.LOCO_ERR_HIP):
+        assert loco.status_string(s).startswith("LOCO_")
+    assert loco.status_string(-99) == "unknown status"
+    assert lib.loco_version() >= 10000
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(loco, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        loco.load("/nonexistent/libloco.so")
+
+
+A = 0x10000  # fake, 16-byte aligned, far-apart device addresses
+Bp, Cp, Dp = 0x20000000, 0x40000000, 0x60000000
+
+
+def seg(g=A, e=Bp, c=Cp, a=Dp, n=1000):
+    return loco.CqSegment(g, e, c, a, n)
+
+
+def cq(lib, segs, gd=F32, ed=F32, bits=4, block=128, beta=0.9, fixed=0.0, nseg=None):
+    arr = (loco.CqSegment * max(1, len(segs)))(*segs) if segs else None
+    return lib.loco_compensate_quantize(arr, len(segs) if nseg is None else nseg, gd, ed, bits, block,
+                                        beta, fixed, None)
+
+
+@pytest.mark.parametrize("kwargs,want", [
+    (dict(nseg=-1), INV),
+    (dict(gd=2), INV), (dict(ed=-1), INV),
+    (dict(bits=0), INV), (dict(bits=9), INV), (dict(bits=3), UNSUP), (dict(bits=1), UNSUP),
+    (dict(beta=-0.1), INV), (dict(beta=1.1), INV), (dict(beta=NAN), INV),
+    (dict(fixed=-1.0), INV), (dict(fixed=math.inf), INV),
+    (dict(block=0), INV), (dict(block=-128), INV), (dict(block=100), UNSUP), (dict(block=1024), UNSUP),
+])
+def test_cq_parameter_checks(lib, kwargs, want):
+    assert cq(lib, [seg()], **kwargs) == want
+
+
+@pytest.mark.parametrize("s,want", [
+    (seg(n=-1), INV),
+    (seg(g=0), INV), (seg(e=0), INV), (seg(c=0), INV), (seg(a=0), INV),
+    (seg(g=A + 2), ALIGN), (seg(e=Bp + 8), ALIGN), (seg(c=Cp + 4), ALIGN), (seg(a=Dp + 4), ALIGN),
+    (seg(e=A + 16), INV),                 # err overlaps grad
+    (seg(c=A + 1000 * 4 - 16), INV),      # codes overlap the last 16 bytes of grad (f32)
+    (seg(a=Cp + 256), INV),               # absmax overlaps codes (500 bytes at 4 bits)
+])
+def test_cq_segment_checks(lib, s, want):
+    assert cq(lib, [s]) == want
+
+
+def test_cq_noop_and_mixed(lib):
+    assert cq(lib, []) == OK
+    assert cq(lib, [seg(n=0), seg(g=0, n=0)]) == OK     # empty segments are never touched
+    # one bad segment refuses the whole call, wherever it is
+    assert cq(lib, [seg(), seg(g=A + 4 * 4096, e=Bp + 4 * 4096, c=Cp + 4096, a=Dp + 4096, n=-5)]) == INV
+    # fixed-scale mode: absmax may be NULL and block is ignored, but everything else is checked
+    assert cq(lib, [seg(a=0, g=A + 2)], fixed=2.0 ** 19, block=7) == ALIGN
+
+
+def pl(c=Cp, a=Dp):
+    return loco.Payload(c, a)
+
+
+def dr(lib, peers, n=1000, bits=4, block=128, fixed=0.0, scale=0.25, out=A, od=F32, npeers=None):
+    arr = (loco.Payload * max(1, len(peers)))(*peers) if peers else None
+    return lib.loco_dequant_reduce(arr, len(peers) if npeers is None else npeers, n, bits, block, fixed,
+                                   scale, out, od, None)
+
+
+@pytest.mark.parametrize("kwargs,want", [
+    (dict(npeers=0), INV), (dict(n=-1), INV), (dict(bits=3), UNSUP), (dict(bits=0), INV),
+    (dict(block=100), UNSUP), (dict(block=0), INV), (dict(fixed=-2.0), INV),
+    (dict(scale=NAN), INV), (dict(scale=math.inf), INV), (dict(od=7), INV),
+    (dict(out=0), INV), (dict(out=A + 4), ALIGN),
+    (dict(out=Cp + 16), INV),             # output overlaps a payload
+])
+def test_dr_checks(lib, kwargs, want):
+    assert dr(lib, [pl(), pl(Cp + 4096, Dp + 4096)], **kwargs) == want
+
+
+def test_dr_peer_checks(lib):
+    assert dr(lib, [pl(c=0)]) == INV
+    assert dr(lib, [pl(a=0)]) == INV
+    assert dr(lib, [pl(c=Cp + 1)]) == ALIGN
+    assert dr(lib, [pl()] * 129) == UNSUP
+    assert dr(lib, [], npeers=1) == INV
+    assert dr(lib, [pl()], n=0) == OK
+
+
+def tk(lib, g=A, e=Bp, n=10000, chunk=4096, k=82, bits=2, decay=1.0, idx=Cp, codes=Dp, absmax=0x70000000):
+    return lib.loco_topk_quantize(g, e, n, chunk, k, bits, decay, idx, codes, absmax, None)
+
+
+@pytest.mark.parametrize("kwargs,want", [
+    (dict(n=-1), INV), (dict(chunk=0), INV), (dict(chunk=70000), INV), (dict(chunk=1000), UNSUP),
+    (dict(chunk=8192), UNSUP), (dict(k=0), INV), (dict(k=4097), INV), (dict(bits=3), UNSUP),
+    (dict(bits=10), INV), (dict(decay=1.5), INV), (dict(decay=NAN), INV),
+    (dict(g=0), INV), (dict(idx=0), INV), (dict(absmax=0), INV),
+    (dict(e=Bp + 4), ALIGN), (dict(codes=Dp + 1), ALIGN),
+    (dict(e=A + 64), INV),                # err overlaps grad
+    (dict(codes=Cp + 16), INV),           # codes overlap the index array
+])
+def test_tk_checks(lib, kwargs, want):
+    assert tk(lib, **kwargs) == want
+
+
+def test_tk_noop(lib):
+    assert tk(lib, n=0) == OK
+    assert tk(lib, n=0, g=0) == OK

@@ -1,0 +1,188 @@
+"""GPU parity of loco_compensate_quantize against the CPU oracle.
+
+Every case runs a free-running chain: the GPU keeps its error buffer, the oracle keeps
+its own, both start from zero and see the same seeded gradients.  Codes and absmax must
+be bit-exact; the error buffer within 1e-6 relative (floor 1e-6 * step) in fp32 or
+1 ulp in bf16 (bitwise equality is expected and reported).  Every output buffer has
+canaries on both sides.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity_util import (Guarded, assert_bf16_close, assert_bytes_equal, assert_f32_close, bf16_bits, host,
+                         say, step_per_elem)
+
+pytestmark = pytest.mark.gpu
+
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+EDGE_SIZES = [1, 0, 7, 8, 9, 511, 512, 513, 1023, 1024, 1025, 4099, 65536 + 17]
+
+
+def grads(step, n, gd, key, scale=None):
+    if gd == "bf16":
+        x = W.shard7b_grad(step, n=n, chain=key)
+    else:
+        x = W.tiny_grad(step, n=n, stream=key)
+    if scale is not None:
+        x = (x.float() * scale).to(TD[gd])
+    return x
+
+
+def storage(t, dt):
+    """CPU tensor -> the oracle's storage form (float32, or uint16 bf16 patterns)."""
+    if dt == "bf16":
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return t.contiguous().numpy()
+
+
+def run_chain(loco, sizes, gd, ed, bits, block, beta, steps, fixed=0.0, gen=None, key="cq"):
+    segs = []
+    for n in sizes:
+        g = Guarded(n, TD[gd])
+        e = Guarded(n, TD[ed], init=torch.zeros(n, dtype=TD[ed]))
+        c = Guarded(loco.code_bytes(n, bits), torch.uint8)
+        a = None if fixed else Guarded(loco.num_blocks(n, block), torch.float32)
+        segs.append((g, e, c, a))
+    e_ora = [np.zeros(n, np.float32 if ed == "f32" else np.uint16) for n in sizes]
+    bitwise = True
+    total = sum(sizes)
+    for step in range(steps):
+        gall = gen(step, total) if gen else grads(step, total, gd, f"{key}-{bits}-{block}")
+        off = 0
+        for (g, _, _, _), n in zip(segs, sizes):
+            g.t.copy_(gall[off:off + n])
+            off += n
+        loco.loco_compensate_quantize([(g.t, e.t, c.t, None if a is None else a.t) for g, e, c, a in segs],
+                                      bits=bits, block=block, beta=beta, fixed_scale=fixed)
+        torch.cuda.synchronize()
+        off = 0
+        for i, ((g, e, c, a), n) in enumerate(zip(segs, sizes)):
+            gn = storage(gall[off:off + n], gd)
+            off += n
+            ref = oracle.compensate_quantize(gn, e_ora[i], bits=bits, block=block, beta=beta,
+                                             fixed_scale=fixed, grad_dtype=gd, err_dtype=ed)
+            tag = f"step {step} segment {i} (n={n})"
+            assert_bytes_equal(host(c.t), ref["codes"], f"{tag} codes")
+            if a is not None:
+                assert_bytes_equal(host(a.t).view(np.uint32), ref["absmax"].view(np.uint32), f"{tag} absmax")
+            if ed == "f32":
+                floor = (step_per_elem(ref["absmax"], bits, block, n) if a is not None
+                         else np.full(n, 1.0 / fixed))
+                bitwise &= assert_f32_close(host(e.t), ref["e_new"], floor, f"{tag} error")
+            else:
+                bitwise &= assert_bf16_close(bf16_bits(e.t), ref["e_new"], f"{tag} error")
+            e_ora[i] = ref["e_new"]
+            for b, nm in zip((g, e, c, a), ("grad", "err", "codes", "absmax")):
+                if b is not None:
+                    b.check(f"{tag} {nm}")
+    return bitwise
+
+
+def test_cq_tiny_workload(gpu_lib):
+    """1,048,576 fp32 ~ N(0, 1e-3), fp32 error, 4-bit, block 128, beta 0.9, 10 steps."""
+    say("cq tiny: n=1048576 f32/f32 4-bit B=128 beta=0.9 x10")
+    bw = run_chain(gpu_lib, [W.TINY_N], "f32", "f32", 4, 128, 0.9, 10,
+                   gen=lambda s, n: W.tiny_grad(s, n=n))
+    say("  error buffer bitwise equal:", bw)
+
+
+@pytest.mark.parametrize("gd", ["f32", "bf16"])
+@pytest.mark.parametrize("ed", ["f32", "bf16"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("block", [64, 128, 256, 512])
+def test_cq_matrix(gpu_lib, gd, ed, bits, block):
+    """Every dtype pair, code width and block size on ragged multi-segment calls."""
+    say(f"cq matrix {gd}/{ed} bits={bits} B={block} sizes={EDGE_SIZES}")
+    run_chain(gpu_lib, EDGE_SIZES, gd, ed, bits, block, 0.9, 2, key="matrix")
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0, 0.99])
+def test_cq_beta(gpu_lib, beta):
+    say(f"cq beta={beta}")
+    run_chain(gpu_lib, [4096 + 5, 300_001], "bf16", "f32", 4, 128, beta, 3, key=f"beta{beta}")
+
+
+@pytest.mark.parametrize("gd", ["f32", "bf16"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("s", [2.0 ** 19, 2.0 ** 17])
+def test_cq_fixed_scale(gpu_lib, gd, bits, s):
+    """Eqn. (1) with the paper's global scale; bf16 inputs near 1e-5 hit exact .5 ties
+    and the clamp at both ends."""
+    say(f"cq fixed scale s={s} {gd} bits={bits}")
+    run_chain(gpu_lib, [1, 1000, 70_001], gd, "f32", bits, 128, 0.9, 3, fixed=s,
+              gen=lambda st, n: grads(st, n, gd, "fixed", scale=1e-2))
+
+
+def test_cq_zero_blocks(gpu_lib):
+    """All-zero blocks and rows keep zero codes, zero absmax and a zero error."""
+    def gen(step, n):
+        x = grads(step, n, "bf16", "zeros").float()
+        x[128:1024] = 0
+        x[5000:9000] = 0
+        x[-300:] = 0
+        return x.to(torch.bfloat16)
+    say("cq zero blocks")
+    run_chain(gpu_lib, [20_000, 333], "bf16", "bf16", 4, 128, 0.9, 3, gen=gen)
+
+
+def test_cq_many_segments(gpu_lib):
+    """75 segments in one call: more than one launch's segment table."""
+    rng = np.random.default_rng(75)
+    sizes = [int(x) for x in rng.integers(0, 3000, 75)]
+    say(f"cq 75 segments, total {sum(sizes)}")
+    run_chain(gpu_lib, sizes, "bf16", "f32", 4, 64, 0.9, 2, key="many")
+
+
+def test_cq_llama_layer_scaled(gpu_lib):
+    """The LLaMA-7B layer recipe with rows / 64: 7 bf16 tensors, fp32 error, 4-bit, B=128."""
+    shapes = W.llama_layer_shapes(64)
+    sizes = [r * c for _, r, c in shapes]
+    say(f"cq llama layer /64: {sizes}")
+    run_chain(gpu_lib, sizes, "bf16", "f32", 4, 128, 0.9, 5,
+              gen=lambda s, n: torch.cat(W.llama_layer_grads(s, div=64)))
+
+
+def test_cq_moe_scaled(gpu_lib):
+    """The MoE recipe with rows / 256: 24 bf16 matrices with 30% zero rows, bf16 error."""
+    shapes = W.moe_shapes(256)
+    sizes = [r * c for _, _, r, c in shapes]
+    say(f"cq moe /256: {len(sizes)} segments")
+    run_chain(gpu_lib, sizes, "bf16", "bf16", 4, 128, 0.9, 3,
+              gen=lambda s, n: torch.cat(W.moe_grads(s, div=256)))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_cq_shard_scaled(gpu_lib, bits):
+    """The 7B-shard recipe at 1/1024 size, split into 8 partitions, B=256."""
+    n = W.SHARD7B_N // 1024
+    part = -(-n // 8)
+    sizes = [part] * 7 + [n - 7 * part]
+    say(f"cq shard /1024 bits={bits} sizes={sizes}")
+    run_chain(gpu_lib, sizes, "bf16", "f32", bits, 256, 0.9, 3,
+              gen=lambda s, m: W.shard7b_grad(s, n=m, chain=f"small{bits}"))
+
+
+def test_cq_deterministic_and_stream(gpu_lib):
+    """Two identical calls give identical bytes, also on a non-default stream."""
+    n = 200_003
+    g = W.shard7b_grad(0, n=n).cuda()
+    outs = []
+    for use_stream in (False, True):
+        e = torch.full((n,), 1e-4, dtype=torch.float32, device="cuda")
+        c = torch.empty(gpu_lib.code_bytes(n, 4), dtype=torch.uint8, device="cuda")
+        a = torch.empty(gpu_lib.num_blocks(n, 256), dtype=torch.float32, device="cuda")
+        st = torch.cuda.Stream() if use_stream else None
+        if st is not None:
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                gpu_lib.loco_compensate_quantize([(g, e, c, a)], bits=4, block=256, beta=0.9)
+            st.synchronize()
+        else:
+            gpu_lib.loco_compensate_quantize([(g, e, c, a)], bits=4, block=256, beta=0.9)
+        torch.cuda.synchronize()
+        outs.append((host(c), host(a), host(e)))
+    for x, y in zip(outs[0], outs[1]):
+        assert np.array_equal(x, y)

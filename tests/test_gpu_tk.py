@@ -1,0 +1,110 @@
+"""GPU parity of loco_topk_quantize (SparseLoCo-style mode) against the CPU oracle.
+
+Indices, codes and absmax must be bit-exact; the error buffer within 1e-6 relative
+(bitwise expected).  Inputs cover the workload's law (Gaussian with exact-tie outliers),
+heavy ties, all-zero chunks, k = 1 and k = chunk, ragged tails and a layout built to push
+the kernel off its fast candidate path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity_util import Guarded, assert_bytes_equal, assert_f32_close, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_tk_chain(loco, n, chunk, k, bits, decay, steps, gen, tag=""):
+    chunks = -(-n // chunk)
+    nb = loco.code_bytes(k, bits)
+    g = Guarded(n, torch.float32)
+    e = Guarded(n, torch.float32, init=torch.zeros(n))
+    idx = Guarded(chunks * k, torch.int16)
+    codes = Guarded(chunks * nb, torch.uint8)
+    am = Guarded(chunks, torch.float32)
+    e_ora = np.zeros(n, np.float32)
+    bw = True
+    for step in range(steps):
+        x = gen(step, n)
+        g.t.copy_(x)
+        loco.loco_topk_quantize(g.t, e.t, chunk=chunk, k=k, idx=idx.t, codes=codes.t, absmax=am.t, bits=bits,
+                                ef_decay=decay)
+        torch.cuda.synchronize()
+        ref = oracle.topk_quantize(x.numpy(), e_ora, chunk=chunk, k=k, bits=bits, decay=decay)
+        t = f"{tag} step {step}"
+        assert_bytes_equal(host(idx.t).view(np.uint16), ref["idx"], f"{t} idx")
+        assert_bytes_equal(host(codes.t), ref["codes"], f"{t} codes")
+        assert_bytes_equal(host(am.t).view(np.uint32), ref["absmax"].view(np.uint32), f"{t} absmax")
+        bw &= assert_f32_close(host(e.t), ref["e_new"], np.repeat(ref["absmax"], chunk)[:n].astype(np.float64),
+                               f"{t} error")
+        e_ora = ref["e_new"]
+        for b, nm in ((g, "grad"), (e, "err"), (idx, "idx"), (codes, "codes"), (am, "absmax")):
+            b.check(f"{t} {nm}")
+    return bw
+
+
+def sparse_gen(step, n):
+    return W.sparseloco_grad(step, n=n)
+
+
+def test_tk_workload_scaled(gpu_lib):
+    """The SparseLoCo workload's law on 40 chunks of 4096 (+ a ragged one), k = 82, 2-bit,
+    decay 1, 5 steps."""
+    say("tk workload scaled: n=40*4096+1234 C=4096 k=82 2-bit x5")
+    assert run_tk_chain(gpu_lib, 40 * 4096 + 1234, 4096, 82, 2, 1.0, 5, sparse_gen, "workload")
+
+
+@pytest.mark.parametrize("chunk", [256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("decay", [1.0, 0.5])
+def test_tk_matrix(gpu_lib, chunk, bits, decay):
+    for k in sorted({1, 3, min(82, chunk), chunk // 2 + 1, chunk}):
+        n = 5 * chunk + chunk // 3 + 1
+        say(f"tk matrix C={chunk} bits={bits} decay={decay} k={k} n={n}")
+        run_tk_chain(gpu_lib, n, chunk, k, bits, decay, 2, sparse_gen, f"C{chunk} k{k}")
+
+
+def ties_gen(step, n):
+    rng = np.random.default_rng(1000 + step)
+    vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0], np.float32)
+    return torch.from_numpy(rng.choice(vals, n).astype(np.float32) * np.float32(1e-3))
+
+
+@pytest.mark.parametrize("k", [1, 5, 82, 128, 129, 600, 4096])
+def test_tk_heavy_ties(gpu_lib, k):
+    """Seven distinct magnitudes: thousands of equal keys; ties go to the lower index."""
+    say(f"tk heavy ties k={k}")
+    run_tk_chain(gpu_lib, 3 * 4096 + 77, 4096, k, 2, 1.0, 3, ties_gen, f"ties k{k}")
+
+
+def test_tk_zero_chunks(gpu_lib):
+    """All-zero chunks keep the first k indices, zero codes, zero absmax."""
+    def gen(step, n):
+        x = W.sparseloco_grad(step, n=n)
+        x[:4096] = 0
+        x[2 * 4096 + 100:] = 0
+        return x
+    say("tk zero chunks")
+    run_tk_chain(gpu_lib, 3 * 4096 + 500, 4096, 82, 2, 1.0, 3, gen, "zeros")
+
+
+def test_tk_fallback_layout(gpu_lib):
+    """Large values only in lanes 0..9 of every slot: the per-lane top-2 bound admits more
+    than the candidate capacity, so the kernel takes its exhaustive path."""
+    def gen(step, n):
+        x = W.sparseloco_grad(step, n=n)
+        i = torch.arange(n)
+        big = (i % 64) < 10
+        x[big] = x[big] * 50 + torch.sign(x[big]) * 0.05
+        return x
+    say("tk fallback layout")
+    run_tk_chain(gpu_lib, 6 * 4096, 4096, 82, 2, 1.0, 3, gen, "fallback")
+
+
+def test_tk_small_tail_only(gpu_lib):
+    """n smaller than one chunk, and k larger than the ragged chunk."""
+    for n in (1, 5, 63, 64, 65, 300):
+        say(f"tk small n={n}")
+        run_tk_chain(gpu_lib, n, 256, 100, 2, 1.0, 2, sparse_gen, f"small n{n}")

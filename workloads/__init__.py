@@ -146,6 +146,22 @@ def moe_grads(step, div=1, experts=8, device="cpu"):
     return out
 
 
+# -- payloads as the dequant-reduce input ---------------------------------------
+
+def random_payload(n, bits, block, key, device="cpu", zero_frac=0.1):
+    """Uniformly random code bytes (padding bits included) and positive absmax values
+    (log-uniform in [1e-5, 1e-2], a fraction of them exactly zero)."""
+    nbytes = (n * bits + 7) // 8
+    g = _gen(device, "payload", key, n, bits, block)
+    codes = torch.randint(0, 256, (nbytes,), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    nb = -(-n // block)
+    u = torch.rand(nb, generator=g, device=device, dtype=torch.float32)
+    absmax = torch.exp(math.log(1e-5) + u * (math.log(1e-2) - math.log(1e-5)))
+    z = torch.rand(nb, generator=g, device=device) < zero_frac
+    absmax[z] = 0.0
+    return codes, absmax
+
+
 # -- SparseLoCo pseudo-gradient -------------------------------------------------
 
 def sparseloco_grad(step, n=SPARSE_N, device="cpu", p_out=1e-3, sigma=1e-3):
