@@ -1,0 +1,285 @@
+"""Benchmark of LoCo's per-GPU gradient path on one MI355X.
+
+A step is one pass of the rank's path on the 7B FSDP-shard workload:
+  compensate-quantize of the rank's 842,000,000-element bf16 gradient (fp32 error,
+  4-bit codes, block 256, beta 0.9), split into 8 partitions of 105,250,000 (one per
+  destination, blocks restarting per partition), then
+  dequant-reduce of the 8 peer payloads of the rank's own partition into bf16 (x 1/8).
+Inputs are resident in HBM before the timed region; the error buffer carries over from
+step to step.  The SparseLoCo-style Top-k mode (2^28 fp32, chunk 4096, k = 82, 2-bit)
+and the 8-bit variant are timed in the same run and reported under "modes".
+
+Prints one JSON line.  value = gradient GB/s = 842,000,000 x 2 bytes / step time.
+roofline: the compensate-quantize kernel's algorithmic bytes / its average launch time
+(HIP events on its stream) against 8 TB/s.  cpu_baseline: the CPU oracle on a bounded
+sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PARTS = 8
+BITS, BLOCK, BETA = 4, 256, 0.9
+TK_CHUNK, TK_K = 4096, 82
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard.json")
+KERNEL_SOURCES = ["bit_gradient_compression_amd/csrc/cq.hip", "bit_gradient_compression_amd/csrc/dr.hip",
+                  "bit_gradient_compression_amd/csrc/tk.hip", "bit_gradient_compression_amd/csrc/loco_device.hpp",
+                  "bit_gradient_compression_amd/csrc/loco_internal.hpp"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cq_bytes(sizes, gs, es, bits, block):
+    return sum(n * (gs + 2 * es) + (n * bits + 7) // 8 + 4 * (-(-n // block)) for n in sizes)
+
+
+def dr_bytes(n, peers, bits, block, out_bytes):
+    return peers * ((n * bits + 7) // 8 + 4 * (-(-n // block))) + n * out_bytes
+
+
+def tk_bytes(n, chunk, k, bits):
+    chunks = -(-n // chunk)
+    return n * 12 + chunks * (2 * k + (k * bits + 7) // 8 + 4)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def load_traffic(kernel_avg_s):
+    """Measured HBM bytes per launch from the committed counter summary, scaled by the
+    plain-copy calibration; None when the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t
+
+
+def cpu_baseline(g_dev, payloads_dev, sample):
+    """The oracle, as it stands, on the first `sample` elements of the rank's shard (one
+    segment, two steps, error carried) and the matching 1/8 of every peer payload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    g = g_dev[:sample].cpu().view(torch.int16).numpy().view(np.uint16)
+    part = sample // PARTS
+    pays = [(c[: (part * BITS + 7) // 8].cpu().numpy(), a[: -(-part // BLOCK)].cpu().numpy())
+            for c, a in payloads_dev]
+    e = np.zeros(sample, np.float32)
+    t0 = time.perf_counter()
+    steps = 2
+    for _ in range(steps):
+        r = oracle.compensate_quantize(g, e, bits=BITS, block=BLOCK, beta=BETA, grad_dtype="bf16")
+        e = r["e_new"]
+        oracle.dequant_reduce(pays, part, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS, out_dtype="bf16")
+    dt = (time.perf_counter() - t0) / steps
+    return {"value": round(sample * 2 / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {sample:,} elements of the shard as one segment + the matching {part:,} elements "
+                      f"of each of the 8 peer payloads, 2 steps; NumPy element-wise, single thread; "
+                      f"{dt:.2f} s per step on {os.cpu_count()} visible cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 23, help="elements of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--no-modes", action="store_true", help="skip the 8-bit and Top-k modes")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (calibrates the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (peers are simulated "
+              "in memory); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from bit_gradient_compression_amd import build as B
+    if not os.path.exists(B.LIB_PATH):
+        B.build()
+    from bit_gradient_compression_amd import loco
+    loco.load()
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    n = W.SHARD7B_N
+    part = W.SHARD7B_PART
+    sizes = [part] * PARTS
+
+    log(f"bench: generating the 7B-shard workload ({n:,} bf16) on {torch.cuda.get_device_name(dev)}")
+    g = W.shard7b_grad(0, n=n, device=dev)
+    e = torch.zeros(n, dtype=torch.float32, device=dev)
+    codes = [torch.empty((part * BITS + 7) // 8 + 16, dtype=torch.uint8, device=dev) for _ in range(PARTS)]
+    absmax = [torch.empty(-(-part // BLOCK), dtype=torch.float32, device=dev) for _ in range(PARTS)]
+    segs = [(g[i * part:(i + 1) * part], e[i * part:(i + 1) * part], codes[i][:(part * BITS + 7) // 8], absmax[i])
+            for i in range(PARTS)]
+
+    # the 8 peer payloads of this rank's partition: each peer quantised its own gradient
+    # (one launch of the same shape as the timed one: 8 segments of 105,250,000)
+    peer_g = W.shard7b_peer_grads(PARTS, n=part, device=dev)
+    peer_e = torch.zeros(n, dtype=torch.float32, device=dev)
+    payloads = [(torch.empty((part * BITS + 7) // 8, dtype=torch.uint8, device=dev),
+                 torch.empty(-(-part // BLOCK), dtype=torch.float32, device=dev)) for _ in range(PARTS)]
+    loco.loco_compensate_quantize([(peer_g[i], peer_e[i * part:(i + 1) * part], *payloads[i]) for i in range(PARTS)],
+                                  bits=BITS, block=BLOCK, beta=BETA)
+    torch.cuda.synchronize()
+    del peer_g, peer_e
+    out = torch.empty(part, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        loco.loco_compensate_quantize(segs, bits=BITS, block=BLOCK, beta=BETA, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        loco.loco_dequant_reduce(payloads, part, bits=BITS, block=BLOCK, out=out, out_scale=1.0 / PARTS,
+                                 stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cq_ms = sorted(ev[0].elapsed_time(ev[1]) for ev in evs)
+    dr_ms = sorted(ev[1].elapsed_time(ev[2]) for ev in evs)
+    avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    ms_per_step = wall * 1e3 / args.steps
+    cq_alg = cq_bytes(sizes, 2, 4, BITS, BLOCK)
+    dr_alg = dr_bytes(part, PARTS, BITS, BLOCK, 2)
+    cq_avg_s = avg(cq_ms) / 1e3
+    dr_avg_s = avg(dr_ms) / 1e3
+    achieved = cq_alg / cq_avg_s / 1e9
+
+    kernels = {
+        "compensate_quantize_4bit": {"avg_ms": round(avg(cq_ms), 4), "p10_ms": round(cq_ms[len(cq_ms) // 10], 4),
+                                     "p90_ms": round(cq_ms[(len(cq_ms) * 9) // 10], 4), "alg_bytes": cq_alg,
+                                     "GBps": round(achieved, 1), "frac_hbm": round(achieved / HBM_PEAK_GBPS, 4)},
+        "dequant_reduce_8peers": {"avg_ms": round(avg(dr_ms), 4), "alg_bytes": dr_alg,
+                                  "GBps": round(dr_alg / dr_avg_s / 1e9, 1),
+                                  "frac_hbm": round(dr_alg / dr_avg_s / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
+
+    traffic = None
+    t = load_traffic(cq_avg_s)
+    if t is not None and "compensate_quantize_4bit" in t.get("kernels", {}):
+        traffic = t["kernels"]["compensate_quantize_4bit"]["hbm_bytes"]
+
+    modes = {}
+    if not args.no_modes:
+        # 8-bit codes on the same shard and error-buffer layout
+        codes8 = [torch.empty(part, dtype=torch.uint8, device=dev) for _ in range(PARTS)]
+        e8 = torch.zeros(n, dtype=torch.float32, device=dev)
+        segs8 = [(g[i * part:(i + 1) * part], e8[i * part:(i + 1) * part], codes8[i], absmax[i])
+                 for i in range(PARTS)]
+        ms = timed(lambda: loco.loco_compensate_quantize(segs8, bits=8, block=BLOCK, beta=BETA, stream=stream),
+                   stream, max(3, args.steps // 3))
+        b8 = cq_bytes(sizes, 2, 4, 8, BLOCK)
+        modes["compensate_quantize_8bit_7b_shard"] = {"avg_ms": round(ms, 4), "alg_bytes": b8,
+                                                      "GBps": round(b8 / ms / 1e6, 1),
+                                                      "frac_hbm": round(b8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                                      "grad_GBps": round(n * 2 / ms / 1e6, 1)}
+        del codes8, e8, segs8
+        # SparseLoCo-style mode on its own workload
+        nt = W.SPARSE_N
+        gt = W.sparseloco_grad(0, n=nt, device=dev)
+        et = torch.zeros(nt, dtype=torch.float32, device=dev)
+        chunks = nt // TK_CHUNK
+        idx = torch.empty(chunks * TK_K, dtype=torch.int16, device=dev)
+        tcodes = torch.empty(chunks * ((TK_K * 2 + 7) // 8), dtype=torch.uint8, device=dev)
+        tabs = torch.empty(chunks, dtype=torch.float32, device=dev)
+        ms = timed(lambda: loco.loco_topk_quantize(gt, et, chunk=TK_CHUNK, k=TK_K, idx=idx, codes=tcodes,
+                                                   absmax=tabs, bits=2, ef_decay=1.0, stream=stream),
+                   stream, max(3, args.steps // 3))
+        bt = tk_bytes(nt, TK_CHUNK, TK_K, 2)
+        modes["sparseloco_topk_2bit"] = {"workload": f"{nt:,} fp32 N(0,1e-3) + 0.1% +-0.1 outliers, chunk 4096, "
+                                                     f"k=82, 2-bit, fp32 error feedback",
+                                         "avg_ms": round(ms, 4), "alg_bytes": bt, "GBps": round(bt / ms / 1e6, 1),
+                                         "frac_hbm": round(bt / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                         "grad_GBps": round(nt * 4 / ms / 1e6, 1)}
+        del gt, et, idx, tcodes, tabs
+
+    cpu = None
+    if args.cpu_sample > 0:
+        log(f"bench: CPU oracle on a {args.cpu_sample:,}-element sample")
+        cpu = cpu_baseline(g, payloads, args.cpu_sample)
+
+    value = n * 2 / (ms_per_step / 1e3) / 1e9
+    line = {
+        "metric": "gradient GB/s through compensate+quantize (and dequant-reduce), % of HBM peak",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "7B FSDP shard: 842,000,000 bf16 grad (1e-3 * Student-t(3)), fp32 error, "
+                               "4-bit block-256 codes in 8 partitions of 105,250,000, beta 0.9; then "
+                               "dequant-reduce of 8 peer 4-bit payloads of 105,250,000 into bf16 x 1/8",
+                   "grad_elems": n, "partitions": PARTS, "bits": BITS, "block": BLOCK, "peers": PARTS,
+                   "peer_elems": part},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "compensate_quantize_4bit", "alg_bytes_per_launch": cq_alg},
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "modes": modes,
+        "pct_hbm_peak_step": round(100 * (cq_alg + dr_alg) / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def timed(fn, stream, reps):
+    import torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+if __name__ == "__main__":
+    main()
