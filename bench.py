@@ -32,15 +32,18 @@ PARTS = 8
 BITS, BLOCK, BETA = 4, 256, 0.9
 TK_CHUNK, TK_K = 4096, 82
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard.json")
-KERNEL_SOURCES = ["bit_gradient_compression_amd/csrc/cq.hip", "bit_gradient_compression_amd/csrc/dr.hip",
-                  "bit_gradient_compression_amd/csrc/tk.hip", "bit_gradient_compression_amd/csrc/loco_device.hpp",
-                  "bit_gradient_compression_amd/csrc/loco_internal.hpp"]
+CSRC = os.path.join(ROOT, "bit_gradient_compression_amd", "csrc")
+KERNEL_FILES = {"compensate_quantize_4bit": ["cq.hip"], "dequant_reduce_8peers": ["dr.hip"],
+                "sparseloco_topk_2bit": ["tk.hip"]}
+COMMON_FILES = ["loco_device.hpp", "loco_internal.hpp"]
 
 
-def source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources a kernel is built from; counter summaries carry it so that a
+    summary taken before the kernel changed is not used."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in KERNEL_FILES[kernel] + COMMON_FILES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -62,42 +65,51 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def load_traffic(kernel_avg_s):
-    """Measured HBM bytes per launch from the committed counter summary, scaled by the
-    plain-copy calibration; None when the kernels changed since it was taken."""
+def load_traffic():
+    """Measured HBM bytes per launch, per kernel, from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration).  A kernel whose
+    sources changed since the counters were taken gets no entry."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("source_hash") != source_hash():
-        return None
-    return t
+        return {}
+    return {k: v for k, v in t.get("kernels", {}).items()
+            if k in KERNEL_FILES and v.get("source_hash") == kernel_source_hash(k)}
 
 
-def cpu_baseline(g_dev, payloads_dev, sample):
-    """The oracle, as it stands, on the first `sample` elements of the rank's shard (one
-    segment, two steps, error carried) and the matching 1/8 of every peer payload."""
+def cpu_baseline(g_dev, payloads_dev, slab, min_seconds=10.0):
+    """The oracle, as it stands, on consecutive slabs of the rank's shard: per slab, two
+    compensate-quantize steps (error carried) on `slab` elements as one segment, and the
+    dequant-reduce of the matching slab/8 elements of every peer payload.  Slabs are
+    added until at least `min_seconds` of oracle time (or the whole shard) is done."""
     import numpy as np
     import torch
 
     import oracle
-    g = g_dev[:sample].cpu().view(torch.int16).numpy().view(np.uint16)
-    part = sample // PARTS
-    pays = [(c[: (part * BITS + 7) // 8].cpu().numpy(), a[: -(-part // BLOCK)].cpu().numpy())
-            for c, a in payloads_dev]
-    e = np.zeros(sample, np.float32)
-    t0 = time.perf_counter()
+    part = slab // PARTS
+    n = g_dev.numel()
+    done = 0
+    spent = 0.0
     steps = 2
-    for _ in range(steps):
-        r = oracle.compensate_quantize(g, e, bits=BITS, block=BLOCK, beta=BETA, grad_dtype="bf16")
-        e = r["e_new"]
-        oracle.dequant_reduce(pays, part, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS, out_dtype="bf16")
-    dt = (time.perf_counter() - t0) / steps
-    return {"value": round(sample * 2 / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {sample:,} elements of the shard as one segment + the matching {part:,} elements "
-                      f"of each of the 8 peer payloads, 2 steps; NumPy element-wise, single thread; "
-                      f"{dt:.2f} s per step on {os.cpu_count()} visible cores"}
+    while done + slab <= n and spent < min_seconds:
+        g = g_dev[done:done + slab].cpu().view(torch.int16).numpy().view(np.uint16)
+        off = done // PARTS
+        pays = [(c[(off * BITS) // 8:((off + part) * BITS + 7) // 8].cpu().numpy(),
+                 a[off // BLOCK:-(-(off + part) // BLOCK)].cpu().numpy()) for c, a in payloads_dev]
+        e = np.zeros(slab, np.float32)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            r = oracle.compensate_quantize(g, e, bits=BITS, block=BLOCK, beta=BETA, grad_dtype="bf16")
+            e = r["e_new"]
+            oracle.dequant_reduce(pays, part, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS, out_dtype="bf16")
+        spent += time.perf_counter() - t0
+        done += slab
+    per_step = spent / steps
+    return {"value": round(done * 2 / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done:,} of the shard's {n:,} elements in slabs of {slab:,} (one segment each) + the "
+                      f"matching 1/8 of each of the 8 peer payloads, 2 steps per slab, {spent:.1f} s of oracle "
+                      f"time; NumPy element-wise, one thread (host shows {os.cpu_count()} cores)"}
 
 
 def main():
@@ -105,7 +117,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample", type=int, default=1 << 23, help="elements of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 23,
+                    help="slab size of the CPU-oracle baseline (0: skip it)")
     ap.add_argument("--no-modes", action="store_true", help="skip the 8-bit and Top-k modes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates the HBM byte counters)")
@@ -201,10 +214,11 @@ def main():
                                   "frac_hbm": round(dr_alg / dr_avg_s / 1e9 / HBM_PEAK_GBPS, 4)},
     }
 
-    traffic = None
-    t = load_traffic(cq_avg_s)
-    if t is not None and "compensate_quantize_4bit" in t.get("kernels", {}):
-        traffic = t["kernels"]["compensate_quantize_4bit"]["hbm_bytes"]
+    measured = load_traffic()
+    traffic = measured.get("compensate_quantize_4bit", {}).get("hbm_bytes")
+    for k, v in measured.items():
+        if k in kernels:
+            kernels[k]["hbm_bytes_measured"] = v["hbm_bytes"]
 
     modes = {}
     if not args.no_modes:
@@ -242,7 +256,7 @@ def main():
 
     cpu = None
     if args.cpu_sample > 0:
-        log(f"bench: CPU oracle on a {args.cpu_sample:,}-element sample")
+        log(f"bench: CPU oracle on slabs of {args.cpu_sample:,} elements (>= 10 s)")
         cpu = cpu_baseline(g, payloads, args.cpu_sample)
 
     value = n * 2 / (ms_per_step / 1e3) / 1e9

@@ -46,15 +46,16 @@ def _run(cmd):
     return r
 
 
-def build(out_path: str = LIB_PATH, extra_flags=(), jobs: int | None = None, verbose=False) -> str:
+def build(out_path: str = LIB_PATH, extra_flags=(), jobs: int | None = None, verbose=False,
+          build_dir: str = BUILD_DIR) -> str:
     """Compile and link the library; returns the path of the .so."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
     flags = compile_flags(extra_flags)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))

@@ -12,22 +12,7 @@
 
 namespace loco {
 
-int device_cus() {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64 && cache[dev] > 0) return cache[dev];
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-    if (dev < 64) cache[dev] = cus;
-    return cus;
-}
-
 namespace {
-
-// Workgroups per compute unit of the persistent streaming grids.
-constexpr int kWgPerCu = 8;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -109,7 +94,6 @@ LOCO_API int loco_compensate_quantize(const loco_cq_segment_t* segs, int nseg,
         p.fixed_inv = fixed_scale;
         p.fixed_step = 1.0f / fixed_scale;
     }
-    const int max_blocks = device_cus() * kWgPerCu;
     hipStream_t st = (hipStream_t)stream;
     int i = 0;
     while (i < nseg) {
@@ -128,8 +112,7 @@ LOCO_API int loco_compensate_quantize(const loco_cq_segment_t* segs, int nseg,
             p.ntiles += (s.n + kCqTile - 1) / kCqTile;
         }
         if (p.nseg == 0) break;
-        if (launch_cq(p, grad_dtype == LOCO_BF16, err_dtype == LOCO_BF16, bits, block, fixed, max_blocks, st) !=
-            hipSuccess)
+        if (launch_cq(p, grad_dtype == LOCO_BF16, err_dtype == LOCO_BF16, bits, block, fixed, st) != hipSuccess)
             return LOCO_ERR_HIP;
     }
     return LOCO_OK;
@@ -173,8 +156,7 @@ LOCO_API int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_
     p.fixed_step = fixed ? 1.0f / fixed_scale : 0.0f;
     p.out_scale = out_scale;
     p.out = out;
-    if (launch_dr(p, bits, block, fixed, out_dtype == LOCO_BF16, device_cus() * kWgPerCu, (hipStream_t)stream) !=
-        hipSuccess)
+    if (launch_dr(p, bits, block, fixed, out_dtype == LOCO_BF16, (hipStream_t)stream) != hipSuccess)
         return LOCO_ERR_HIP;
     return LOCO_OK;
 }

@@ -5,11 +5,12 @@
 // averages their decompressed values in high precision:
 //   acc = sum over p = 0..N-1 (in that order) of q_p * step_p;  out = acc * out_scale
 //
-// Mapping: lane l of a wavefront owns 32 consecutive outputs, so each peer's codes for
-// the lane are one 16-byte load at 4 bits (8 bytes at 2 bits, 32 at 8 bits) and the
-// 32 outputs sit in one scale block (blocks are >= 64 elements).  The fp32
-// accumulator never leaves registers; only the reduced shard is written.  The grid is
-// persistent and grid-strides over wave tiles of 2048 elements.
+// Mapping: a wave tile is kDrUnroll sub-tiles of 512 outputs; lane l owns 8 consecutive
+// outputs of each sub-tile, so every load of a peer's codes (4 bytes at 4 bits) and every
+// store of outputs (16 bytes of bf16, 32 of fp32) is contiguous across the wave and the
+// written lines are whole.  The 8 outputs of a lane sit in one scale block (blocks are
+// >= 64 elements).  The fp32 accumulator never leaves registers; only the reduced shard
+// is written.  One wave tile per wave, the grid covering all tiles.
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"
@@ -17,27 +18,20 @@
 namespace loco {
 namespace {
 
+// Codes of 8 consecutive elements (element i0 is a multiple of 8): 2, 4 or 8 bytes.
 template <int BITS>
-__device__ __forceinline__ int field(const uint32_t (&w)[kDrVec * BITS / 32], int j) {
-    constexpr int PER = 32 / BITS;  // codes per 32-bit word
-    return __builtin_amdgcn_sbfe(w[j / PER], (j % PER) * BITS, BITS);
+__device__ __forceinline__ u32x2 load_codes8(const uint8_t* c, int64_t i0) {
+    const uint8_t* p = c + (i0 * BITS) / 8;
+    if constexpr (BITS == 2) return u32x2{(uint32_t)__builtin_nontemporal_load((const uint16_t*)p), 0u};
+    else if constexpr (BITS == 4) return u32x2{__builtin_nontemporal_load((const uint32_t*)p), 0u};
+    else return __builtin_nontemporal_load((const u32x2*)p);
 }
 
+// Signed code j (0..7) of the 8 held in w.
 template <int BITS>
-__device__ __forceinline__ void load_codes(const uint8_t* c, int64_t i0, uint32_t (&w)[kDrVec * BITS / 32]) {
-    const uint8_t* p = c + (i0 * BITS) / 8;
-    if constexpr (BITS == 2) {
-        u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
-        w[0] = v.x; w[1] = v.y;
-    } else if constexpr (BITS == 4) {
-        u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
-        u32x4 a = __builtin_nontemporal_load((const u32x4*)p);
-        u32x4 b = __builtin_nontemporal_load((const u32x4*)p + 1);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    }
+__device__ __forceinline__ int code_of(u32x2 w, int j) {
+    if constexpr (BITS == 8) return __builtin_amdgcn_sbfe(j < 4 ? w.x : w.y, (j & 3) * 8, 8);
+    else return __builtin_amdgcn_sbfe(w.x, j * BITS, BITS);
 }
 
 template <int BITS, int B, bool FIXED>
@@ -47,73 +41,87 @@ __device__ __forceinline__ float peer_step(const DrPeerDev& pe, int64_t i0, floa
     else return pe.absmax[i0 / B] / (float)QMAX;  // 0 for an all-zero block
 }
 
+template <bool OBF>
+__device__ __forceinline__ void store_out8(void* out, int64_t i0, const float (&acc)[kDrVec], float scale) {
+    if constexpr (OBF) {
+        u32x4 s;
+        s.x = bf16x2_rne(acc[0] * scale, acc[1] * scale);
+        s.y = bf16x2_rne(acc[2] * scale, acc[3] * scale);
+        s.z = bf16x2_rne(acc[4] * scale, acc[5] * scale);
+        s.w = bf16x2_rne(acc[6] * scale, acc[7] * scale);
+        __builtin_nontemporal_store(s, (u32x4*)((uint16_t*)out + i0));
+    } else {
+        f32x4* o = (f32x4*)((float*)out + i0);
+        f32x4 a = {acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale};
+        f32x4 b = {acc[4] * scale, acc[5] * scale, acc[6] * scale, acc[7] * scale};
+        __builtin_nontemporal_store(a, o);
+        __builtin_nontemporal_store(b, o + 1);
+    }
+}
+
 template <int BITS, int B, bool FIXED, bool OBF>
 __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
-    constexpr int NW = kDrVec * BITS / 32;
+    constexpr int SUB = 64 * kDrVec;
     const int lane = lane_id();
-    const int64_t wave0 = (int64_t)blockIdx.x * (kDrThreads / kWave) + uniform(threadIdx.x / kWave);
     const int64_t nwaves = (int64_t)gridDim.x * (kDrThreads / kWave);
-    for (int64_t t = wave0; t < p.ntiles; t += nwaves) {
-        const int64_t i0 = t * kDrTile + lane * kDrVec;
-        float acc[kDrVec];
+    const int64_t wg = xcd_remap<kXcds, kDrXcdRun>(blockIdx.x, gridDim.x);
+    for (int64_t t = wg * (kDrThreads / kWave) + uniform(threadIdx.x / kWave); t < p.ntiles;
+         t += nwaves) {
+        const int64_t base = t * kDrTile + lane * kDrVec;
+        float acc[kDrUnroll][kDrVec];
 #pragma unroll
-        for (int j = 0; j < kDrVec; ++j) acc[j] = 0.0f;
+        for (int u = 0; u < kDrUnroll; ++u)
+#pragma unroll
+            for (int j = 0; j < kDrVec; ++j) acc[u][j] = 0.0f;
 
         if ((t + 1) * kDrTile <= p.n) {
             // whole wave tile in range
 #pragma unroll 2
             for (int pi = 0; pi < p.npeers; ++pi) {
                 const DrPeerDev pe = p.peer[pi];
-                uint32_t w[NW];
-                load_codes<BITS>(pe.codes, i0, w);
-                const float step = peer_step<BITS, B, FIXED>(pe, i0, p.fixed_step);
+                u32x2 w[kDrUnroll];
+                float step[kDrUnroll];
 #pragma unroll
-                for (int j = 0; j < kDrVec; ++j) acc[j] = acc[j] + (float)field<BITS>(w, j) * step;
-            }
-            if constexpr (OBF) {
-                uint16_t* o = (uint16_t*)p.out + i0;
-#pragma unroll
-                for (int v = 0; v < kDrVec / 8; ++v) {
-                    u32x4 s;
-                    s.x = bf16x2_rne(acc[8 * v + 0] * p.out_scale, acc[8 * v + 1] * p.out_scale);
-                    s.y = bf16x2_rne(acc[8 * v + 2] * p.out_scale, acc[8 * v + 3] * p.out_scale);
-                    s.z = bf16x2_rne(acc[8 * v + 4] * p.out_scale, acc[8 * v + 5] * p.out_scale);
-                    s.w = bf16x2_rne(acc[8 * v + 6] * p.out_scale, acc[8 * v + 7] * p.out_scale);
-                    __builtin_nontemporal_store(s, (u32x4*)(o + 8 * v));
+                for (int u = 0; u < kDrUnroll; ++u) {
+                    w[u] = load_codes8<BITS>(pe.codes, base + u * SUB);
+                    step[u] = peer_step<BITS, B, FIXED>(pe, base + u * SUB, p.fixed_step);
                 }
-            } else {
-                float* o = (float*)p.out + i0;
 #pragma unroll
-                for (int v = 0; v < kDrVec / 4; ++v) {
-                    f32x4 s = {acc[4 * v] * p.out_scale, acc[4 * v + 1] * p.out_scale,
-                               acc[4 * v + 2] * p.out_scale, acc[4 * v + 3] * p.out_scale};
-                    __builtin_nontemporal_store(s, (f32x4*)(o + 4 * v));
-                }
+                for (int u = 0; u < kDrUnroll; ++u)
+#pragma unroll
+                    for (int j = 0; j < kDrVec; ++j)
+                        acc[u][j] = acc[u][j] + (float)code_of<BITS>(w[u], j) * step[u];
             }
+#pragma unroll
+            for (int u = 0; u < kDrUnroll; ++u) store_out8<OBF>(p.out, base + u * SUB, acc[u], p.out_scale);
         } else {
             // ragged tail: element-wise, reading only the bytes that exist
-            const int64_t left = p.n - i0;
-            const int nvalid = left <= 0 ? 0 : (left >= kDrVec ? kDrVec : (int)left);
-            if (nvalid == 0) continue;
-            for (int pi = 0; pi < p.npeers; ++pi) {
-                const DrPeerDev pe = p.peer[pi];
-                const float step = peer_step<BITS, B, FIXED>(pe, i0, p.fixed_step);
+#pragma unroll
+            for (int u = 0; u < kDrUnroll; ++u) {
+                const int64_t i0 = base + u * SUB;
+                const int64_t left = p.n - i0;
+                const int nvalid = left <= 0 ? 0 : (left >= kDrVec ? kDrVec : (int)left);
+                if (nvalid == 0) continue;
+                for (int pi = 0; pi < p.npeers; ++pi) {
+                    const DrPeerDev pe = p.peer[pi];
+                    const float step = peer_step<BITS, B, FIXED>(pe, i0, p.fixed_step);
+#pragma unroll
+                    for (int j = 0; j < kDrVec; ++j) {
+                        if (j < nvalid) {
+                            const int64_t i = i0 + j;
+                            const uint32_t byte = pe.codes[(i * BITS) / 8];
+                            const int q = __builtin_amdgcn_sbfe(byte, (int)((i * BITS) % 8), BITS);
+                            acc[u][j] = acc[u][j] + (float)q * step;
+                        }
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < kDrVec; ++j) {
                     if (j < nvalid) {
-                        const int64_t i = i0 + j;
-                        const uint32_t byte = pe.codes[(i * BITS) / 8];
-                        const int q = __builtin_amdgcn_sbfe(byte, (int)((i * BITS) % 8), BITS);
-                        acc[j] = acc[j] + (float)q * step;
+                        const float v = acc[u][j] * p.out_scale;
+                        if constexpr (OBF) ((uint16_t*)p.out)[i0 + j] = bf16_rne(v);
+                        else ((float*)p.out)[i0 + j] = v;
                     }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < kDrVec; ++j) {
-                if (j < nvalid) {
-                    const float v = acc[j] * p.out_scale;
-                    if constexpr (OBF) ((uint16_t*)p.out)[i0 + j] = bf16_rne(v);
-                    else ((float*)p.out)[i0 + j] = v;
                 }
             }
         }
@@ -148,14 +156,14 @@ const void* pick_bits(int bits, int block) {
 }  // namespace
 
 hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, bool out_bf16,
-                     int max_blocks, hipStream_t stream) {
+                     hipStream_t stream) {
     const void* k = nullptr;
     if (fixed) k = out_bf16 ? pick_bits<true, true>(bits, block) : pick_bits<true, false>(bits, block);
     else k = out_bf16 ? pick_bits<false, true>(bits, block) : pick_bits<false, false>(bits, block);
     if (!k) return hipErrorInvalidValue;
     const int64_t waves_per_block = kDrThreads / kWave;
     int64_t blocks = (p.ntiles + waves_per_block - 1) / waves_per_block;
-    if (blocks > max_blocks) blocks = max_blocks;
+    if (blocks > kMaxGrid) blocks = kMaxGrid;
     if (blocks < 1) blocks = 1;
     void* args[] = {(void*)&p};
     return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(kDrThreads), args, 0, stream);

@@ -77,6 +77,21 @@ __device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
     return m ? __builtin_ctzll(m) : 63;
 }
 
+// Logical workgroup number of physical workgroup b out of g: groups of RUN consecutive
+// logical numbers share one XCD (dispatch is round-robin over NX XCDs).  Workgroups of an
+// incomplete last group keep their own number.
+template <int NX, int RUN>
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t g) {
+    if constexpr (RUN <= 1) {
+        return b;
+    } else {
+        constexpr int64_t SPAN = (int64_t)NX * RUN;
+        if (b >= g - g % SPAN) return b;
+        const int64_t x = b % NX, r = b / NX;
+        return (r / RUN) * SPAN + x * RUN + (r % RUN);
+    }
+}
+
 // Wave-uniform value as an SGPR.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

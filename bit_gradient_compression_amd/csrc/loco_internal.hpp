@@ -8,13 +8,48 @@ namespace loco {
 
 // ---- compensate-quantize -----------------------------------------------------------
 
+// Launch shape of the streaming kernels.  The grid is not persistent: each wave takes one
+// tile and exits, so the waves in flight sweep memory in address order; the grid-stride
+// loop only matters past kMaxGrid workgroups.
+#ifndef LOCO_CQ_UNROLL
+#define LOCO_CQ_UNROLL 1
+#endif
+#ifndef LOCO_CQ_THREADS
+#define LOCO_CQ_THREADS 256
+#endif
+#ifndef LOCO_DR_UNROLL
+#define LOCO_DR_UNROLL 2
+#endif
+#ifndef LOCO_DR_THREADS
+#define LOCO_DR_THREADS 256
+#endif
+#ifndef LOCO_TK_WAVES_PER_EU
+#define LOCO_TK_WAVES_PER_EU 1
+#endif
+#ifndef LOCO_CQ_XCD_RUN
+#define LOCO_CQ_XCD_RUN 32
+#endif
+#ifndef LOCO_DR_XCD_RUN
+#define LOCO_DR_XCD_RUN 1
+#endif
+constexpr int64_t kMaxGrid = (int64_t)1 << 22;
+// Workgroups are dispatched round-robin over the chip's 8 XCDs (each with its own L2).
+// The streaming kernels renumber their workgroups so that runs of consecutive logical
+// workgroups execute on one XCD (1: identity).  Measured on MI355X for compensate-
+// quantize: runs of ~128 waves (32 workgroups of 256 threads) per XCD move the fused
+// kernel from ~68% to ~71.5% of peak HBM bandwidth; short runs (16-32 waves) are slower
+// than the identity.
+constexpr int kXcds = 8;
+constexpr int kCqXcdRun = LOCO_CQ_XCD_RUN;
+constexpr int kDrXcdRun = LOCO_DR_XCD_RUN;
+
 // Segments per launch; a call with more segments is split into several launches.
 constexpr int kCqMaxSeg = 32;
 // Elements per lane per sub-tile, and sub-tiles per wave tile.
 constexpr int kCqVec = 8;
-constexpr int kCqUnroll = 2;
+constexpr int kCqUnroll = LOCO_CQ_UNROLL;
 constexpr int kCqTile = 64 * kCqVec * kCqUnroll;  // elements per wave tile
-constexpr int kCqThreads = 256;
+constexpr int kCqThreads = LOCO_CQ_THREADS;
 
 struct CqSegDev {
     const void* g;
@@ -34,14 +69,15 @@ struct CqParams {
 };
 
 hipError_t launch_cq(const CqParams& p, bool grad_bf16, bool err_bf16, int bits, int block,
-                     bool fixed, int max_blocks, hipStream_t stream);
+                     bool fixed, hipStream_t stream);
 
 // ---- dequant-reduce ---------------------------------------------------------------
 
 constexpr int kDrMaxPeers = 128;
-constexpr int kDrVec = 32;                 // elements per lane
-constexpr int kDrTile = 64 * kDrVec;       // elements per wave tile
-constexpr int kDrThreads = 256;
+constexpr int kDrVec = 8;                          // consecutive outputs per lane per sub-tile
+constexpr int kDrUnroll = LOCO_DR_UNROLL;          // sub-tiles per wave tile
+constexpr int kDrTile = 64 * kDrVec * kDrUnroll;   // elements per wave tile
+constexpr int kDrThreads = LOCO_DR_THREADS;
 
 struct DrPeerDev {
     const uint8_t* codes;
@@ -59,7 +95,7 @@ struct DrParams {
 };
 
 hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, bool out_bf16,
-                     int max_blocks, hipStream_t stream);
+                     hipStream_t stream);
 
 // ---- chunked Top-k ----------------------------------------------------------------
 
@@ -80,8 +116,5 @@ struct TkParams {
 };
 
 hipError_t launch_tk(const TkParams& p, int chunk, int bits, hipStream_t stream);
-
-// Compute units of the current device (cached per device).
-int device_cus();
 
 }  // namespace loco

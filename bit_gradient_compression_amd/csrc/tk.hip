@@ -28,6 +28,7 @@ __device__ __forceinline__ uint32_t key_of(float h) { return __float_as_uint(h) 
 template <int VPT, int BITS>
 __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint32_t* s_key,
                                          uint16_t* s_idx, uint8_t* s_code) {
+    static_assert(VPT <= 64, "one sign bit per slot in a 64-bit mask");
     constexpr int C = 64 * VPT;
     constexpr int QMAX = (1 << (BITS - 1)) - 1;
     constexpr int NSLOT = kTkCap / 64;
@@ -38,29 +39,29 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint3
     const int keff = p.k < len ? p.k : len;
     const bool full = (len == C);
 
-    // h = g + decay * e
-    float h[VPT];
-    if (full) {
+    // h = g + decay * e, kept as its key bits(|h|) plus one sign bit per slot.  Elements
+    // past the end of a short chunk get key 0: every threshold tried below is >= 1, and
+    // among equal keys the lower index wins, so they are never selected ahead of a real
+    // element (keff <= len).
+    uint32_t kv[VPT];
+    uint64_t sgn = 0;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int64_t i = base + j * 64 + lane;
-            h[j] = __builtin_nontemporal_load(p.g + i) + p.decay * p.e[i];
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int i = j * 64 + lane;
-            h[j] = (i < len) ? p.g[base + i] + p.decay * p.e[base + i] : 0.0f;
-        }
+    for (int j = 0; j < VPT; ++j) {
+        const int64_t i = base + j * 64 + lane;
+        float h = 0.0f;
+        if (full) h = __builtin_nontemporal_load(p.g + i) + p.decay * p.e[i];
+        else if (j * 64 + lane < len) h = p.g[i] + p.decay * p.e[i];
+        const uint32_t u = __float_as_uint(h);
+        kv[j] = u & 0x7FFFFFFFu;
+        sgn |= (uint64_t)(u >> 31) << j;
     }
 
     // per-lane two largest keys, chunk max
     uint32_t m1 = 0, m2 = 0;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-        const uint32_t kk = key_of(h[j]);
-        const uint32_t lo = min(m1, kk);
-        m1 = max(m1, kk);
+        const uint32_t lo = min(m1, kv[j]);
+        m1 = max(m1, kv[j]);
         m2 = max(m2, lo);
     }
     const uint32_t M = (uint32_t)uniform((int)wave_max_u32(m1));
@@ -81,15 +82,13 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint3
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int i = j * 64 + lane;
-            const uint32_t kk = key_of(h[j]);
-            const bool c = (i < len) && kk >= L;
+            const bool c = kv[j] >= L;
             const uint64_t b = ballot(c);
             if (c) {
                 const int pos = cnt + mbcnt(b);
                 if (pos < kTkCap) {
-                    s_key[pos] = kk;
-                    s_idx[pos] = (uint16_t)i;
+                    s_key[pos] = kv[j];
+                    s_idx[pos] = (uint16_t)(j * 64 + lane);
                 }
             }
             cnt += __popcll(b);
@@ -98,32 +97,30 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint3
             __syncthreads();
             const int nslots = (cnt + 63) / 64;
             uint32_t cv[NSLOT];
-            bool ok[NSLOT];
 #pragma unroll
             for (int s = 0; s < NSLOT; ++s) {
                 const int pos = s * 64 + lane;
-                ok[s] = pos < cnt;
-                cv[s] = ok[s] ? s_key[pos] : 0u;
+                cv[s] = pos < cnt ? s_key[pos] : 0u;
             }
-            // 3. T = keff-th largest candidate
+            // 3. T = keff-th largest candidate (padding 0 never reaches a threshold >= 1)
             for (int bit = 30; bit >= 0; --bit) {
                 const uint32_t cand = T | (1u << bit);
                 int c = 0;
 #pragma unroll
                 for (int s = 0; s < NSLOT; ++s)
-                    if (s < nslots) c += __popcll(ballot(ok[s] && cv[s] >= cand));
+                    if (s < nslots) c += __popcll(ballot(cv[s] >= cand));
                 if (c >= keff) T = cand;
             }
             int gt = 0;
 #pragma unroll
             for (int s = 0; s < NSLOT; ++s)
-                if (s < nslots) gt += __popcll(ballot(ok[s] && cv[s] > T));
+                if (s < nslots) gt += __popcll(ballot(cv[s] > T));
             need = keff - gt;
             int seen = 0;
 #pragma unroll
             for (int s = 0; s < NSLOT; ++s) {
                 if (s < nslots && ilast < 0) {
-                    const uint64_t b = ballot(ok[s] && cv[s] == T);
+                    const uint64_t b = ballot(s * 64 + lane < cnt && cv[s] == T);
                     const int pc = __popcll(b);
                     if (seen + pc >= need) ilast = uniform((int)s_idx[s * 64 + nth_set_bit(b, need - seen)]);
                     seen += pc;
@@ -139,18 +136,18 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint3
             const uint32_t cand = T | (1u << bit);
             int c = 0;
 #pragma unroll
-            for (int j = 0; j < VPT; ++j) c += __popcll(ballot((j * 64 + lane) < len && key_of(h[j]) >= cand));
+            for (int j = 0; j < VPT; ++j) c += __popcll(ballot(kv[j] >= cand));
             if (c >= keff) T = cand;
         }
         int gt = 0;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) gt += __popcll(ballot((j * 64 + lane) < len && key_of(h[j]) > T));
+        for (int j = 0; j < VPT; ++j) gt += __popcll(ballot(kv[j] > T));
         need = keff - gt;
         int seen = 0;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             if (ilast < 0) {
-                const uint64_t b = ballot((j * 64 + lane) < len && key_of(h[j]) == T);
+                const uint64_t b = ballot(kv[j] == T);
                 const int pc = __popcll(b);
                 if (seen + pc >= need) ilast = j * 64 + nth_set_bit(b, need - seen);
                 seen += pc;
@@ -167,14 +164,14 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint3
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         const int i = j * 64 + lane;
-        const uint32_t kk = key_of(h[j]);
-        const bool sel = (i < len) && (kk > T || (kk == T && i <= ilast));
-        const float rq = __builtin_amdgcn_fmed3f(__builtin_rintf(h[j] * inv), (float)(-QMAX - 1), (float)QMAX);
+        const float h = __uint_as_float(kv[j] | ((uint32_t)(sgn >> j) & 1u) << 31);
+        // keys above T are real elements; ties are kept up to index ilast (< len)
+        const bool sel = kv[j] > T || (kv[j] == T && i <= ilast);
+        const float rq = __builtin_amdgcn_fmed3f(__builtin_rintf(h * inv), (float)(-QMAX - 1), (float)QMAX);
         const int q = (int)rq;
         const float d = (float)q * step;
-        const float en = sel ? h[j] - d : h[j];
-        if (full) p.e[base + i] = en;
-        else if (i < len) p.e[base + i] = en;
+        const float en = sel ? h - d : h;
+        if (full || i < len) p.e[base + i] = en;
         const uint64_t b = ballot(sel);
         if (sel) {
             // pos < keff when the selection is right; the guard keeps a wrong selection
@@ -207,7 +204,8 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint3
 // Grid-strides over chunks; the barrier at the end of each chunk lets the next one
 // reuse the LDS staging arrays.
 template <int VPT, int BITS>
-__global__ __launch_bounds__(64) void tk_kernel(TkParams p, int64_t nchunks) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(LOCO_TK_WAVES_PER_EU)))
+void tk_kernel(TkParams p, int64_t nchunks) {
     __shared__ uint32_t s_key[kTkCap];
     __shared__ uint16_t s_idx[kTkCap];
     __shared__ uint8_t s_code[64 * VPT];
