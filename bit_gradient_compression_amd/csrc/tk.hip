@@ -2,20 +2,22 @@
 // error feedback ("Communication Efficient LLM Pre-training with SparseLoCo": Top-k
 // sparsification, 2-bit quantisation, error feedback).
 //
-// One wavefront (one 64-thread workgroup) owns one chunk of C = 64*VPT elements held
-// in registers, element j*64 + lane in slot j, so every global access is a 256-byte
-// coalesced row and ballot order within a slot is index order.
+// One 256-thread workgroup (4 waves) owns one chunk of C = 256*VPT elements; element
+// i = 256*j + 64*w + lane sits in slot j of lane `lane` of wave w, so every global access
+// is a 256-byte coalesced row per wave and (slot, wave, lane) order is index order.
+// Each element is held as its key bits(|h|) plus one sign bit, VPT keys per lane.
 //
-// Exact selection of the k-th largest key T = bits(|h|) (ties to the lower index):
-//  1. each lane keeps its two largest keys; the k-th largest of those 128 keys, L, is
-//     a lower bound of T (k of the chunk's keys are >= L);
-//  2. the chunk's keys >= L (about k + a few) are compacted, in index order, into LDS;
-//  3. T is found among them bit by bit (31 ballot/popcount rounds over a few slots),
-//     with the count of keys > T and the index of the last tie that is kept.
-// If k > 128 or more than kTkCap keys are >= L (adversarial layouts), step 3 runs over
-// all registers instead.  Either way the result is the same exact set.
-// The kept elements are then compacted in index order (ballot + mbcnt), their codes
-// staged in LDS and packed, and the new error is written for every element.
+// Exact selection of the k-th largest key T (ties to the lower index):
+//  1. the k-th largest of the 256 per-thread maxima is a lower bound L of T (k keys of
+//     the chunk are >= L);
+//  2. the keys >= L (about k + a few) are compacted in index order into LDS (per-wave
+//     ballot counts, a cross-wave prefix over (slot, wave) pairs, then mbcnt);
+//  3. wave 0 finds T among them bit by bit (31 ballot/popcount rounds), with the count
+//     of keys above T and the index of the last tie that is kept.
+// If k > 256 or more than kTkCap keys are >= L, all four waves search every key instead
+// (cross-wave counts through LDS); the result is the same exact set.
+// The kept elements are then compacted in index order the same way, their codes staged
+// in LDS and packed, and the new error is written for every element.
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"
@@ -23,148 +25,226 @@
 namespace loco {
 namespace {
 
-__device__ __forceinline__ uint32_t key_of(float h) { return __float_as_uint(h) & 0x7FFFFFFFu; }
+constexpr int kTkThreads = 256;
+constexpr int kTkWaves = kTkThreads / kWave;
+
+struct TkShared {
+    uint32_t top[kTkThreads];   // per-thread maximum key
+    uint32_t key[kTkCap];       // candidate keys, index order
+    uint16_t idx[kTkCap];       // their chunk-local indices
+    int cnt[64];                // per (slot, wave) counts, pair p = 4*slot + wave
+    uint32_t wmax[kTkWaves];
+    int red[kTkWaves];
+    uint32_t L, T;
+    int ilast;
+    uint8_t code[4096];         // kept codes, index order (k <= C <= 4096)
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(v, d, 64);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix of sh.cnt over the 4*VPT (slot, wave) pairs, lane p holding pair p;
+// `total` is the sum over all pairs.
+template <int VPT>
+__device__ __forceinline__ int pair_prefix(const TkShared& sh, int lane, int& total) {
+    constexpr int NP = kTkWaves * VPT;
+    const int v = lane < NP ? sh.cnt[lane] : 0;
+    const int incl = wave_incl_scan(v, lane);
+    total = __builtin_amdgcn_readlane(incl, 63);
+    return incl - v;
+}
 
 template <int VPT, int BITS>
-__device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint32_t* s_key,
-                                         uint16_t* s_idx, uint8_t* s_code) {
-    static_assert(VPT <= 64, "one sign bit per slot in a 64-bit mask");
-    constexpr int C = 64 * VPT;
+__device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkShared& sh) {
+    static_assert(VPT <= 16, "C <= 4096");
+    constexpr int C = kTkThreads * VPT;
+    constexpr int NP = kTkWaves * VPT;
     constexpr int QMAX = (1 << (BITS - 1)) - 1;
     constexpr int NSLOT = kTkCap / 64;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = uniform(tid >> 6);
     const int64_t base = chunk * C;
     const int64_t rem = p.n - base;
     const int len = rem < C ? (int)rem : C;
     const int keff = p.k < len ? p.k : len;
     const bool full = (len == C);
 
-    // h = g + decay * e, kept as its key bits(|h|) plus one sign bit per slot.  Elements
-    // past the end of a short chunk get key 0: every threshold tried below is >= 1, and
-    // among equal keys the lower index wins, so they are never selected ahead of a real
-    // element (keff <= len).
+    // A. h = g + decay * e as key + sign; elements past the end of a short chunk get key 0,
+    //    which no threshold tried below (>= 1) admits and which loses every tie to a real
+    //    element of lower index (keff <= len).
     uint32_t kv[VPT];
-    uint64_t sgn = 0;
+    uint32_t sgn = 0;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-        const int64_t i = base + j * 64 + lane;
+        const int i = j * kTkThreads + tid;
         float h = 0.0f;
-        if (full) h = __builtin_nontemporal_load(p.g + i) + p.decay * p.e[i];
-        else if (j * 64 + lane < len) h = p.g[i] + p.decay * p.e[i];
+        if (full) h = __builtin_nontemporal_load(p.g + base + i) + p.decay * p.e[base + i];
+        else if (i < len) h = p.g[base + i] + p.decay * p.e[base + i];
         const uint32_t u = __float_as_uint(h);
         kv[j] = u & 0x7FFFFFFFu;
-        sgn |= (uint64_t)(u >> 31) << j;
+        sgn |= (u >> 31) << j;
     }
-
-    // per-lane two largest keys, chunk max
-    uint32_t m1 = 0, m2 = 0;
+    uint32_t m1 = 0;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const uint32_t lo = min(m1, kv[j]);
-        m1 = max(m1, kv[j]);
-        m2 = max(m2, lo);
-    }
-    const uint32_t M = (uint32_t)uniform((int)wave_max_u32(m1));
+    for (int j = 0; j < VPT; ++j) m1 = max(m1, kv[j]);
+    const uint32_t wm = wave_max_u32(m1);
+    if (lane == 0) sh.wmax[w] = wm;
+    sh.top[tid] = m1;
+    __syncthreads();
+    const uint32_t M = max(max(sh.wmax[0], sh.wmax[1]), max(sh.wmax[2], sh.wmax[3]));
 
-    uint32_t T = 0;
-    int need = 0, ilast = -1;
-    bool done = false;
-
-    if (keff <= 128) {
-        // 1. lower bound L from the per-lane top-2 keys
-        uint32_t L = 0;
-        for (int bit = 30; bit >= 0; --bit) {
-            const uint32_t cand = L | (1u << bit);
-            const int c = __popcll(ballot(m1 >= cand)) + __popcll(ballot(m2 >= cand));
-            if (c >= keff) L = cand;
+    // B. lower bound L: the keff-th largest per-thread maximum (wave 0)
+    const bool try_fast = keff <= kTkThreads;
+    bool fast = false;
+    if (try_fast) {
+        if (w == 0) {
+            const uint32_t t0 = sh.top[lane], t1 = sh.top[lane + 64], t2 = sh.top[lane + 128],
+                           t3 = sh.top[lane + 192];
+            uint32_t L = 0;
+            for (int bit = 30; bit >= 0; --bit) {
+                const uint32_t cand = L | (1u << bit);
+                const int c = __popcll(ballot(t0 >= cand)) + __popcll(ballot(t1 >= cand)) +
+                              __popcll(ballot(t2 >= cand)) + __popcll(ballot(t3 >= cand));
+                if (c >= keff) L = cand;
+            }
+            if (lane == 0) sh.L = L;
         }
-        // 2. compact the keys >= L in index order
-        int cnt = 0;
+        __syncthreads();
+
+        // C. compact the keys >= L in index order
+        const uint32_t L = sh.L;
+        uint64_t cb[VPT];
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const bool c = kv[j] >= L;
-            const uint64_t b = ballot(c);
-            if (c) {
-                const int pos = cnt + mbcnt(b);
-                if (pos < kTkCap) {
-                    s_key[pos] = kv[j];
-                    s_idx[pos] = (uint16_t)(j * 64 + lane);
+            cb[j] = ballot(kv[j] >= L);
+            if (lane == 0) sh.cnt[j * kTkWaves + w] = __popcll(cb[j]);
+        }
+        __syncthreads();
+        int total = 0;
+        const int excl = pair_prefix<VPT>(sh, lane, total);
+        if (total <= kTkCap) {
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                // read the pair's base in uniform control flow: a lane read inside the
+                // divergent branch below could be an inactive one
+                const int bj = __builtin_amdgcn_readlane(excl, j * kTkWaves + w);
+                if (kv[j] >= L) {
+                    const int pos = bj + mbcnt(cb[j]);
+                    sh.key[pos] = kv[j];
+                    sh.idx[pos] = (uint16_t)(j * kTkThreads + tid);
                 }
             }
-            cnt += __popcll(b);
+            fast = true;
         }
-        if (cnt <= kTkCap) {
-            __syncthreads();
-            const int nslots = (cnt + 63) / 64;
-            uint32_t cv[NSLOT];
+        __syncthreads();
+
+        // D (fast). T, the count above it and the last kept tie, among the candidates
+        if (fast) {
+            if (w == 0) {
+                const int nslots = (total + 63) / 64;
+                uint32_t cv[NSLOT];
 #pragma unroll
-            for (int s = 0; s < NSLOT; ++s) {
-                const int pos = s * 64 + lane;
-                cv[s] = pos < cnt ? s_key[pos] : 0u;
-            }
-            // 3. T = keff-th largest candidate (padding 0 never reaches a threshold >= 1)
-            for (int bit = 30; bit >= 0; --bit) {
-                const uint32_t cand = T | (1u << bit);
-                int c = 0;
+                for (int s = 0; s < NSLOT; ++s) {
+                    const int pos = s * 64 + lane;
+                    cv[s] = (s < nslots && pos < total) ? sh.key[pos] : 0u;
+                }
+                uint32_t T = 0;
+                for (int bit = 30; bit >= 0; --bit) {
+                    const uint32_t cand = T | (1u << bit);
+                    int c = 0;
+#pragma unroll
+                    for (int s = 0; s < NSLOT; ++s)
+                        if (s < nslots) c += __popcll(ballot(cv[s] >= cand));
+                    if (c >= keff) T = cand;
+                }
+                int gt = 0;
 #pragma unroll
                 for (int s = 0; s < NSLOT; ++s)
-                    if (s < nslots) c += __popcll(ballot(cv[s] >= cand));
-                if (c >= keff) T = cand;
-            }
-            int gt = 0;
+                    if (s < nslots) gt += __popcll(ballot(cv[s] > T));
+                const int need = keff - gt;
+                int seen = 0, ilast = -1;
 #pragma unroll
-            for (int s = 0; s < NSLOT; ++s)
-                if (s < nslots) gt += __popcll(ballot(cv[s] > T));
-            need = keff - gt;
-            int seen = 0;
-#pragma unroll
-            for (int s = 0; s < NSLOT; ++s) {
-                if (s < nslots && ilast < 0) {
-                    const uint64_t b = ballot(s * 64 + lane < cnt && cv[s] == T);
-                    const int pc = __popcll(b);
-                    if (seen + pc >= need) ilast = uniform((int)s_idx[s * 64 + nth_set_bit(b, need - seen)]);
-                    seen += pc;
+                for (int s = 0; s < NSLOT; ++s) {
+                    if (s < nslots && ilast < 0) {
+                        const uint64_t b = ballot(s * 64 + lane < total && cv[s] == T);
+                        const int pc = __popcll(b);
+                        if (seen + pc >= need) ilast = uniform((int)sh.idx[s * 64 + nth_set_bit(b, need - seen)]);
+                        seen += pc;
+                    }
+                }
+                if (lane == 0) {
+                    sh.T = T;
+                    sh.ilast = ilast;
                 }
             }
-            done = true;
+            __syncthreads();
         }
     }
 
-    if (!done) {
-        // exact search over every key of the chunk
+    if (!fast) {
+        // D (exhaustive). All waves search every key; counts meet in LDS.
+        uint32_t T = 0;
         for (int bit = 30; bit >= 0; --bit) {
             const uint32_t cand = T | (1u << bit);
             int c = 0;
 #pragma unroll
             for (int j = 0; j < VPT; ++j) c += __popcll(ballot(kv[j] >= cand));
+            if (lane == 0) sh.red[w] = c;
+            __syncthreads();
+            c = sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3];
+            __syncthreads();
             if (c >= keff) T = cand;
         }
         int gt = 0;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) gt += __popcll(ballot(kv[j] > T));
-        need = keff - gt;
-        int seen = 0;
+        if (lane == 0) sh.red[w] = gt;
+        uint64_t tb[VPT];
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            if (ilast < 0) {
-                const uint64_t b = ballot(kv[j] == T);
-                const int pc = __popcll(b);
-                if (seen + pc >= need) ilast = j * 64 + nth_set_bit(b, need - seen);
-                seen += pc;
+            tb[j] = ballot(kv[j] == T);
+            if (lane == 0) sh.cnt[j * kTkWaves + w] = __popcll(tb[j]);
+        }
+        __syncthreads();
+        const int need = keff - (sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3]);
+        int total = 0;
+        const int excl = pair_prefix<VPT>(sh, lane, total);
+        // the first (slot, wave) pair whose running tie count reaches `need` holds the last
+        // kept tie
+        const int mine = lane < NP ? sh.cnt[lane] : 0;
+        const uint64_t reach = ballot(lane < NP && excl + mine >= need);
+        const int pstar = reach ? __builtin_ctzll(reach) : 0;
+        const int before = __builtin_amdgcn_readlane(excl, pstar);
+        if (w == pstar % kTkWaves && lane == 0) {
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                if (j == pstar / kTkWaves) sh.ilast = j * kTkThreads + w * 64 + nth_set_bit(tb[j], need - before);
             }
         }
+        if (tid == 0) sh.T = T;
+        __syncthreads();
     }
 
-    // quantise the kept values with the chunk's absmax; error feedback for all
+    // E. quantise the kept values with the chunk's absmax; error feedback for all
+    const uint32_t T = sh.T;
+    const int ilast = sh.ilast;
     const float absmax = __uint_as_float(M);
     const float step = absmax / (float)QMAX;
     const float inv = (M != 0u) ? 1.0f / step : 0.0f;
-    uint16_t* idx_out = p.idx + chunk * p.k;
-    int cum = 0;
+    uint64_t sb[VPT];
+    int qv[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-        const int i = j * 64 + lane;
-        const float h = __uint_as_float(kv[j] | ((uint32_t)(sgn >> j) & 1u) << 31);
+        const int i = j * kTkThreads + tid;
+        const float h = __uint_as_float(kv[j] | ((sgn >> j) & 1u) << 31);
         // keys above T are real elements; ties are kept up to index ilast (< len)
         const bool sel = kv[j] > T || (kv[j] == T && i <= ilast);
         const float rq = __builtin_amdgcn_fmed3f(__builtin_rintf(h * inv), (float)(-QMAX - 1), (float)QMAX);
@@ -172,45 +252,53 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, uint3
         const float d = (float)q * step;
         const float en = sel ? h - d : h;
         if (full || i < len) p.e[base + i] = en;
-        const uint64_t b = ballot(sel);
-        if (sel) {
-            // pos < keff when the selection is right; the guard keeps a wrong selection
-            // from writing outside this chunk's slots
-            const int pos = cum + mbcnt(b);
-            if (pos < keff) {
-                idx_out[pos] = (uint16_t)i;
-                s_code[pos] = (uint8_t)((uint32_t)q & ((1u << BITS) - 1u));
-            }
-        }
-        cum += __popcll(b);
+        sb[j] = ballot(sel);
+        qv[j] = q;
+        if (lane == 0) sh.cnt[j * kTkWaves + w] = __popcll(sb[j]);
     }
     __syncthreads();
-    for (int pos = keff + lane; pos < p.k; pos += 64) idx_out[pos] = 0xFFFF;
+    int total = 0;
+    const int excl = pair_prefix<VPT>(sh, lane, total);
+    uint16_t* idx_out = p.idx + chunk * p.k;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int bj = __builtin_amdgcn_readlane(excl, j * kTkWaves + w);  // uniform control flow
+        if ((sb[j] >> lane) & 1u) {
+            // pos < keff when the selection is right; the guard keeps a wrong selection from
+            // writing outside this chunk's slots
+            const int pos = bj + mbcnt(sb[j]);
+            if (pos < keff) {
+                idx_out[pos] = (uint16_t)(j * kTkThreads + tid);
+                sh.code[pos] = (uint8_t)((uint32_t)qv[j] & ((1u << BITS) - 1u));
+            }
+        }
+    }
+    __syncthreads();
+
+    // F. unused slots, packed codes, scale
+    for (int pos = keff + tid; pos < p.k; pos += kTkThreads) idx_out[pos] = 0xFFFF;
     constexpr int PER = 8 / BITS;
     const int nbytes = (p.k * BITS + 7) / 8;
     uint8_t* codes_out = p.codes + chunk * nbytes;
-    for (int b = lane; b < nbytes; b += 64) {
+    for (int b = tid; b < nbytes; b += kTkThreads) {
         uint32_t v = 0;
 #pragma unroll
         for (int t = 0; t < PER; ++t) {
             const int pos = b * PER + t;
-            if (pos < keff) v |= (uint32_t)s_code[pos] << (BITS * t);
+            if (pos < keff) v |= (uint32_t)sh.code[pos] << (BITS * t);
         }
         codes_out[b] = (uint8_t)v;
     }
-    if (lane == 0) p.absmax[chunk] = absmax;
+    if (tid == 0) p.absmax[chunk] = absmax;
 }
 
-// Grid-strides over chunks; the barrier at the end of each chunk lets the next one
-// reuse the LDS staging arrays.
+// Grid-strides over chunks; the barrier at the end of each chunk lets the next one reuse
+// the LDS staging.
 template <int VPT, int BITS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(LOCO_TK_WAVES_PER_EU)))
-void tk_kernel(TkParams p, int64_t nchunks) {
-    __shared__ uint32_t s_key[kTkCap];
-    __shared__ uint16_t s_idx[kTkCap];
-    __shared__ uint8_t s_code[64 * VPT];
+__global__ __launch_bounds__(kTkThreads) void tk_kernel(TkParams p, int64_t nchunks) {
+    __shared__ TkShared sh;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        tk_chunk<VPT, BITS>(p, c, s_key, s_idx, s_code);
+        tk_chunk<VPT, BITS>(p, c, sh);
         __syncthreads();
     }
 }
@@ -218,11 +306,11 @@ void tk_kernel(TkParams p, int64_t nchunks) {
 template <int BITS>
 const void* pick_chunk(int chunk) {
     switch (chunk) {
-        case 256: return (const void*)&tk_kernel<4, BITS>;
-        case 512: return (const void*)&tk_kernel<8, BITS>;
-        case 1024: return (const void*)&tk_kernel<16, BITS>;
-        case 2048: return (const void*)&tk_kernel<32, BITS>;
-        case 4096: return (const void*)&tk_kernel<64, BITS>;
+        case 256: return (const void*)&tk_kernel<1, BITS>;
+        case 512: return (const void*)&tk_kernel<2, BITS>;
+        case 1024: return (const void*)&tk_kernel<4, BITS>;
+        case 2048: return (const void*)&tk_kernel<8, BITS>;
+        case 4096: return (const void*)&tk_kernel<16, BITS>;
     }
     return nullptr;
 }
@@ -240,7 +328,7 @@ hipError_t launch_tk(const TkParams& p, int chunk, int bits, hipStream_t stream)
     int64_t chunks = (p.n + chunk - 1) / chunk;
     const int64_t grid = chunks < kTkMaxGrid ? chunks : kTkMaxGrid;
     void* args[] = {(void*)&p, (void*)&chunks};
-    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(64), args, 0, stream);
+    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(kTkThreads), args, 0, stream);
 }
 
 }  // namespace loco
