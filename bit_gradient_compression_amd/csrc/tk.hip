@@ -8,12 +8,13 @@
 // Each element is held as its key bits(|h|) plus one sign bit, VPT keys per lane.
 //
 // Exact selection of the k-th largest key T (ties to the lower index):
-//  1. the k-th largest of the 256 per-thread maxima is a lower bound L of T (k keys of
-//     the chunk are >= L);
-//  2. the keys >= L (about k + a few) are compacted in index order into LDS (per-wave
-//     ballot counts, a cross-wave prefix over (slot, wave) pairs, then mbcnt);
-//  3. wave 0 finds T among them bit by bit (31 ballot/popcount rounds), with the count
-//     of keys above T and the index of the last tie that is kept.
+//  1. a lower bound L of T: the largest value with 12 significant key bits (exponent and
+//     4 mantissa bits) that at least k per-thread maxima reach (12 ballot rounds, wave 0);
+//     k keys of the chunk are then >= L;
+//  2. the keys >= L (about k + a few dozen) are compacted in index order into LDS
+//     (per-wave ballot counts, a cross-wave prefix over (slot, wave) pairs, then mbcnt);
+//  3. every thread ranks its candidate against all candidates (16-byte broadcast LDS
+//     reads); the candidate of rank k-1 gives T and the index of the last tie kept.
 // If k > 256 or more than kTkCap keys are >= L, all four waves search every key instead
 // (cross-wave counts through LDS); the result is the same exact set.
 // The kept elements are then compacted in index order the same way, their codes staged
@@ -27,10 +28,12 @@ namespace {
 
 constexpr int kTkThreads = 256;
 constexpr int kTkWaves = kTkThreads / kWave;
+// The lower bound L keeps key bits 30..kTkBoundLowBit (exponent + 4 mantissa bits).
+constexpr int kTkBoundLowBit = 19;
 
 struct TkShared {
     uint32_t top[kTkThreads];   // per-thread maximum key
-    uint32_t key[kTkCap];       // candidate keys, index order
+    alignas(16) uint32_t key[kTkCap + 4];  // candidate keys, index order, zero-padded to a 16-byte row
     uint16_t idx[kTkCap];       // their chunk-local indices
     int cnt[64];                // per (slot, wave) counts, pair p = 4*slot + wave
     uint32_t wmax[kTkWaves];
@@ -61,36 +64,46 @@ __device__ __forceinline__ int pair_prefix(const TkShared& sh, int lane, int& to
     return incl - v;
 }
 
-template <int VPT, int BITS>
+// FULL: the chunk has all C elements (every chunk but a short last one); the loads and
+// stores of a full chunk are straight-line code, so all of them are in flight at once.
+template <int VPT, int BITS, bool FULL>
 __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkShared& sh) {
     static_assert(VPT <= 16, "C <= 4096");
     constexpr int C = kTkThreads * VPT;
     constexpr int NP = kTkWaves * VPT;
     constexpr int QMAX = (1 << (BITS - 1)) - 1;
-    constexpr int NSLOT = kTkCap / 64;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = uniform(tid >> 6);
     const int64_t base = chunk * C;
     const int64_t rem = p.n - base;
-    const int len = rem < C ? (int)rem : C;
+    const int len = FULL ? C : (rem < C ? (int)rem : C);
     const int keff = p.k < len ? p.k : len;
-    const bool full = (len == C);
 
     // A. h = g + decay * e as key + sign; elements past the end of a short chunk get key 0,
     //    which no threshold tried below (>= 1) admits and which loses every tie to a real
     //    element of lower index (keff <= len).
     uint32_t kv[VPT];
     uint32_t sgn = 0;
+    {
+        float gv[VPT], ev[VPT];
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int i = j * kTkThreads + tid;
-        float h = 0.0f;
-        if (full) h = __builtin_nontemporal_load(p.g + base + i) + p.decay * p.e[base + i];
-        else if (i < len) h = p.g[base + i] + p.decay * p.e[base + i];
-        const uint32_t u = __float_as_uint(h);
-        kv[j] = u & 0x7FFFFFFFu;
-        sgn |= (u >> 31) << j;
+        for (int j = 0; j < VPT; ++j) {
+            const int i = j * kTkThreads + tid;
+            if (FULL) {
+                gv[j] = __builtin_nontemporal_load(p.g + base + i);
+                ev[j] = p.e[base + i];
+            } else {
+                gv[j] = i < len ? p.g[base + i] : 0.0f;
+                ev[j] = i < len ? p.e[base + i] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const uint32_t u = __float_as_uint(gv[j] + p.decay * ev[j]);
+            kv[j] = u & 0x7FFFFFFFu;
+            sgn |= (u >> 31) << j;
+        }
     }
     uint32_t m1 = 0;
 #pragma unroll
@@ -108,8 +121,9 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
         if (w == 0) {
             const uint32_t t0 = sh.top[lane], t1 = sh.top[lane + 64], t2 = sh.top[lane + 128],
                            t3 = sh.top[lane + 192];
+            // only a bound is needed: search the exponent and the top 4 mantissa bits
             uint32_t L = 0;
-            for (int bit = 30; bit >= 0; --bit) {
+            for (int bit = 30; bit >= kTkBoundLowBit; --bit) {
                 const uint32_t cand = L | (1u << bit);
                 const int c = __popcll(ballot(t0 >= cand)) + __popcll(ballot(t1 >= cand)) +
                               __popcll(ballot(t2 >= cand)) + __popcll(ballot(t3 >= cand));
@@ -142,47 +156,31 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
                     sh.idx[pos] = (uint16_t)(j * kTkThreads + tid);
                 }
             }
+            if (tid < 4 && total + tid < kTkCap + 4) sh.key[total + tid] = 0u;
             fast = true;
         }
         __syncthreads();
 
-        // D (fast). T, the count above it and the last kept tie, among the candidates
+        // D (fast). Every thread ranks its own candidate(s) against all candidates in the
+        // order (key descending, index ascending): rank = #{keys above} + #{equal keys at
+        // lower positions}.  Ranks are a permutation of 0..total-1, so the candidate of
+        // rank keff-1 is the last kept element: its key is T and, T being its key, its
+        // index is the last kept tie.
         if (fast) {
-            if (w == 0) {
-                const int nslots = (total + 63) / 64;
-                uint32_t cv[NSLOT];
-#pragma unroll
-                for (int s = 0; s < NSLOT; ++s) {
-                    const int pos = s * 64 + lane;
-                    cv[s] = (s < nslots && pos < total) ? sh.key[pos] : 0u;
+            const int nrow = (total + 3) >> 2;
+            for (int t = tid; t < total; t += kTkThreads) {
+                const uint32_t mk = sh.key[t];
+                int rank = 0;
+                for (int r = 0; r < nrow; ++r) {
+                    const u32x4 kr = *(const u32x4*)&sh.key[4 * r];
+                    const int c = 4 * r;
+                    rank += (kr.x > mk) + (kr.y > mk) + (kr.z > mk) + (kr.w > mk);
+                    rank += (kr.x == mk && c < t) + (kr.y == mk && c + 1 < t) + (kr.z == mk && c + 2 < t) +
+                            (kr.w == mk && c + 3 < t);
                 }
-                uint32_t T = 0;
-                for (int bit = 30; bit >= 0; --bit) {
-                    const uint32_t cand = T | (1u << bit);
-                    int c = 0;
-#pragma unroll
-                    for (int s = 0; s < NSLOT; ++s)
-                        if (s < nslots) c += __popcll(ballot(cv[s] >= cand));
-                    if (c >= keff) T = cand;
-                }
-                int gt = 0;
-#pragma unroll
-                for (int s = 0; s < NSLOT; ++s)
-                    if (s < nslots) gt += __popcll(ballot(cv[s] > T));
-                const int need = keff - gt;
-                int seen = 0, ilast = -1;
-#pragma unroll
-                for (int s = 0; s < NSLOT; ++s) {
-                    if (s < nslots && ilast < 0) {
-                        const uint64_t b = ballot(s * 64 + lane < total && cv[s] == T);
-                        const int pc = __popcll(b);
-                        if (seen + pc >= need) ilast = uniform((int)sh.idx[s * 64 + nth_set_bit(b, need - seen)]);
-                        seen += pc;
-                    }
-                }
-                if (lane == 0) {
-                    sh.T = T;
-                    sh.ilast = ilast;
+                if (rank == keff - 1) {
+                    sh.T = mk;
+                    sh.ilast = sh.idx[t];
                 }
             }
             __syncthreads();
@@ -251,7 +249,7 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
         const int q = (int)rq;
         const float d = (float)q * step;
         const float en = sel ? h - d : h;
-        if (full || i < len) p.e[base + i] = en;
+        if (FULL || i < len) p.e[base + i] = en;
         sb[j] = ballot(sel);
         qv[j] = q;
         if (lane == 0) sh.cnt[j * kTkWaves + w] = __popcll(sb[j]);
@@ -298,7 +296,8 @@ template <int VPT, int BITS>
 __global__ __launch_bounds__(kTkThreads) void tk_kernel(TkParams p, int64_t nchunks) {
     __shared__ TkShared sh;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        tk_chunk<VPT, BITS>(p, c, sh);
+        if ((c + 1) * (kTkThreads * VPT) <= p.n) tk_chunk<VPT, BITS, true>(p, c, sh);
+        else tk_chunk<VPT, BITS, false>(p, c, sh);
         __syncthreads();
     }
 }
