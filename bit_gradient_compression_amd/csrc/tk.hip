@@ -7,18 +7,21 @@
 // is a 256-byte coalesced row per wave and (slot, wave, lane) order is index order.
 // Each element is held as its key bits(|h|) plus one sign bit, VPT keys per lane.
 //
-// Exact selection of the k-th largest key T (ties to the lower index):
-//  1. a lower bound L of T: the largest value with 12 significant key bits (exponent and
-//     4 mantissa bits) that at least k per-thread maxima reach (12 ballot rounds, wave 0);
-//     k keys of the chunk are then >= L;
+// Exact selection of the k kept elements (largest keys, ties to the lower index):
+//  1. a lower bound L of the k-th largest key: the largest value with 12 significant key
+//     bits (exponent and 4 mantissa bits) that at least k per-thread maxima reach
+//     (12 ballot rounds, wave 0); k keys of the chunk are then >= L;
 //  2. the keys >= L (about k + a few dozen) are compacted in index order into LDS
 //     (per-wave ballot counts, a cross-wave prefix over (slot, wave) pairs, then mbcnt);
-//  3. every thread ranks its candidate against all candidates (16-byte broadcast LDS
-//     reads); the candidate of rank k-1 gives T and the index of the last tie kept.
+//  3. every thread ranks its candidate against all candidates in the order (key
+//     descending, index ascending) with 16-byte broadcast LDS reads; the kept elements
+//     are exactly the candidates of rank < k, already in index order.  Their threads
+//     quantise them, write their error, index and code; the candidate of rank k-1 gives
+//     the threshold T and the last kept tie;
+//  4. every other element's error is h, written by a masked store.
 // If k > 256 or more than kTkCap keys are >= L, all four waves search every key instead
-// (cross-wave counts through LDS); the result is the same exact set.
-// The kept elements are then compacted in index order the same way, their codes staged
-// in LDS and packed, and the new error is written for every element.
+// (cross-wave counts through LDS) and every element is selected and compacted in place;
+// the result is the same exact set.
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"
@@ -32,15 +35,16 @@ constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkBoundLowBit = 19;
 
 struct TkShared {
-    uint32_t top[kTkThreads];   // per-thread maximum key
-    alignas(16) uint32_t key[kTkCap + 4];  // candidate keys, index order, zero-padded to a 16-byte row
-    uint16_t idx[kTkCap];       // their chunk-local indices
-    int cnt[64];                // per (slot, wave) counts, pair p = 4*slot + wave
+    uint32_t top[kTkThreads];               // per-thread maximum key
+    alignas(16) uint32_t key[kTkCap + 4];   // candidate keys, index order, zero-padded to a 16-byte row
+    uint32_t hb[kTkCap];                    // candidate h bit patterns
+    uint16_t idx[kTkCap];                   // candidate chunk-local indices
+    int cnt[64];                            // per (slot, wave) counts, pair p = 4*slot + wave
     uint32_t wmax[kTkWaves];
     int red[kTkWaves];
     uint32_t L, T;
     int ilast;
-    uint8_t code[4096];         // kept codes, index order (k <= C <= 4096)
+    uint8_t code[4096];                     // kept codes, index order (k <= C <= 4096)
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -53,15 +57,23 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Exclusive prefix of sh.cnt over the 4*VPT (slot, wave) pairs, lane p holding pair p;
-// `total` is the sum over all pairs.
-template <int VPT>
+// Exclusive prefix of sh.cnt[0..NP) held by lane p for pair p; `total` is the sum.
+template <int NP>
 __device__ __forceinline__ int pair_prefix(const TkShared& sh, int lane, int& total) {
-    constexpr int NP = kTkWaves * VPT;
     const int v = lane < NP ? sh.cnt[lane] : 0;
     const int incl = wave_incl_scan(v, lane);
     total = __builtin_amdgcn_readlane(incl, 63);
     return incl - v;
+}
+
+template <int BITS>
+__device__ __forceinline__ int quantise(float h, float inv) {
+    constexpr int QMAX = (1 << (BITS - 1)) - 1;
+    return (int)__builtin_amdgcn_fmed3f(__builtin_rintf(h * inv), (float)(-QMAX - 1), (float)QMAX);
+}
+
+__device__ __forceinline__ float h_of(uint32_t key, uint32_t sgn, int j) {
+    return __uint_as_float(key | ((sgn >> j) & 1u) << 31);
 }
 
 // FULL: the chunk has all C elements (every chunk but a short last one); the loads and
@@ -72,6 +84,7 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
     constexpr int C = kTkThreads * VPT;
     constexpr int NP = kTkWaves * VPT;
     constexpr int QMAX = (1 << (BITS - 1)) - 1;
+    constexpr uint32_t CMASK = (1u << BITS) - 1u;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = uniform(tid >> 6);
@@ -79,6 +92,7 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
     const int64_t rem = p.n - base;
     const int len = FULL ? C : (rem < C ? (int)rem : C);
     const int keff = p.k < len ? p.k : len;
+    uint16_t* idx_out = p.idx + chunk * p.k;
 
     // A. h = g + decay * e as key + sign; elements past the end of a short chunk get key 0,
     //    which no threshold tried below (>= 1) admits and which loses every tie to a real
@@ -112,16 +126,18 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
     if (lane == 0) sh.wmax[w] = wm;
     sh.top[tid] = m1;
     __syncthreads();
+    // the chunk's absmax is its largest key, always kept (keff >= 1)
     const uint32_t M = max(max(sh.wmax[0], sh.wmax[1]), max(sh.wmax[2], sh.wmax[3]));
+    const float absmax = __uint_as_float(M);
+    const float step = absmax / (float)QMAX;
+    const float inv = (M != 0u) ? 1.0f / step : 0.0f;
 
-    // B. lower bound L: the keff-th largest per-thread maximum (wave 0)
-    const bool try_fast = keff <= kTkThreads;
     bool fast = false;
-    if (try_fast) {
+    if (keff <= kTkThreads) {
+        // B. lower bound L (wave 0)
         if (w == 0) {
             const uint32_t t0 = sh.top[lane], t1 = sh.top[lane + 64], t2 = sh.top[lane + 128],
                            t3 = sh.top[lane + 192];
-            // only a bound is needed: search the exponent and the top 4 mantissa bits
             uint32_t L = 0;
             for (int bit = 30; bit >= kTkBoundLowBit; --bit) {
                 const uint32_t cand = L | (1u << bit);
@@ -135,60 +151,94 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
 
         // C. compact the keys >= L in index order
         const uint32_t L = sh.L;
-        uint64_t cb[VPT];
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            cb[j] = ballot(kv[j] >= L);
-            if (lane == 0) sh.cnt[j * kTkWaves + w] = __popcll(cb[j]);
+            const int c = __popcll(ballot(kv[j] >= L));
+            if (lane == 0) sh.cnt[j * kTkWaves + w] = c;
         }
         __syncthreads();
         int total = 0;
-        const int excl = pair_prefix<VPT>(sh, lane, total);
+        const int excl = pair_prefix<NP>(sh, lane, total);
         if (total <= kTkCap) {
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 // read the pair's base in uniform control flow: a lane read inside the
                 // divergent branch below could be an inactive one
                 const int bj = __builtin_amdgcn_readlane(excl, j * kTkWaves + w);
+                const uint64_t b = ballot(kv[j] >= L);  // taken again rather than kept: SGPRs are short
                 if (kv[j] >= L) {
-                    const int pos = bj + mbcnt(cb[j]);
+                    const int pos = bj + mbcnt(b);
                     sh.key[pos] = kv[j];
+                    sh.hb[pos] = kv[j] | ((sgn >> j) & 1u) << 31;
                     sh.idx[pos] = (uint16_t)(j * kTkThreads + tid);
                 }
             }
-            if (tid < 4 && total + tid < kTkCap + 4) sh.key[total + tid] = 0u;
+            if (tid < 4) sh.key[total + tid] = 0u;
             fast = true;
         }
         __syncthreads();
 
-        // D (fast). Every thread ranks its own candidate(s) against all candidates in the
-        // order (key descending, index ascending): rank = #{keys above} + #{equal keys at
-        // lower positions}.  Ranks are a permutation of 0..total-1, so the candidate of
-        // rank keff-1 is the last kept element: its key is T and, T being its key, its
-        // index is the last kept tie.
         if (fast) {
+            // D. rank every candidate; keep rank < keff
             const int nrow = (total + 3) >> 2;
-            for (int t = tid; t < total; t += kTkThreads) {
-                const uint32_t mk = sh.key[t];
-                int rank = 0;
-                for (int r = 0; r < nrow; ++r) {
-                    const u32x4 kr = *(const u32x4*)&sh.key[4 * r];
-                    const int c = 4 * r;
-                    rank += (kr.x > mk) + (kr.y > mk) + (kr.z > mk) + (kr.w > mk);
-                    rank += (kr.x == mk && c < t) + (kr.y == mk && c + 1 < t) + (kr.z == mk && c + 2 < t) +
-                            (kr.w == mk && c + 3 < t);
+            uint64_t selb[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int t = s * kTkThreads + tid;
+                bool kept = false;
+                if (s * kTkThreads + 64 * w < total) {
+                    const uint32_t mk = sh.key[t];
+                    int rank = 0;
+                    for (int r = 0; r < nrow; ++r) {
+                        const u32x4 kr = *(const u32x4*)&sh.key[4 * r];
+                        const int c = 4 * r;
+                        rank += (kr.x > mk) + (kr.y > mk) + (kr.z > mk) + (kr.w > mk);
+                        rank += (kr.x == mk && c < t) + (kr.y == mk && c + 1 < t) + (kr.z == mk && c + 2 < t) +
+                                (kr.w == mk && c + 3 < t);
+                    }
+                    kept = t < total && rank < keff;
+                    if (t < total && rank == keff - 1) {
+                        sh.T = mk;
+                        sh.ilast = sh.idx[t];
+                    }
                 }
-                if (rank == keff - 1) {
-                    sh.T = mk;
-                    sh.ilast = sh.idx[t];
+                selb[s] = ballot(kept);
+                if (lane == 0) sh.cnt[s * kTkWaves + w] = __popcll(selb[s]);
+            }
+            __syncthreads();
+            int nkept = 0;
+            const int kex = pair_prefix<2 * kTkWaves>(sh, lane, nkept);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int bs = __builtin_amdgcn_readlane(kex, s * kTkWaves + w);  // uniform control flow
+                if ((selb[s] >> lane) & 1u) {
+                    const int t = s * kTkThreads + tid;
+                    const int pos = bs + mbcnt(selb[s]);
+                    const float h = __uint_as_float(sh.hb[t]);
+                    const int i = sh.idx[t];
+                    const int q = quantise<BITS>(h, inv);
+                    p.e[base + i] = h - (float)q * step;
+                    if (pos < keff) {
+                        idx_out[pos] = (uint16_t)i;
+                        sh.code[pos] = (uint8_t)((uint32_t)q & CMASK);
+                    }
                 }
             }
             __syncthreads();
+            // E. every element that is not kept keeps its whole h as error
+            const uint32_t T = sh.T;
+            const int ilast = sh.ilast;
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int i = j * kTkThreads + tid;
+                const bool kept = kv[j] > T || (kv[j] == T && i <= ilast);
+                if (!kept && (FULL || i < len)) p.e[base + i] = h_of(kv[j], sgn, j);
+            }
         }
     }
 
     if (!fast) {
-        // D (exhaustive). All waves search every key; counts meet in LDS.
+        // D'. exhaustive: all waves search every key; counts meet in LDS
         uint32_t T = 0;
         for (int bit = 30; bit >= 0; --bit) {
             const uint32_t cand = T | (1u << bit);
@@ -205,69 +255,61 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
 #pragma unroll
         for (int j = 0; j < VPT; ++j) gt += __popcll(ballot(kv[j] > T));
         if (lane == 0) sh.red[w] = gt;
-        uint64_t tb[VPT];
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            tb[j] = ballot(kv[j] == T);
-            if (lane == 0) sh.cnt[j * kTkWaves + w] = __popcll(tb[j]);
+            const int c = __popcll(ballot(kv[j] == T));
+            if (lane == 0) sh.cnt[j * kTkWaves + w] = c;
         }
         __syncthreads();
         const int need = keff - (sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3]);
-        int total = 0;
-        const int excl = pair_prefix<VPT>(sh, lane, total);
+        int ties = 0;
+        const int excl = pair_prefix<NP>(sh, lane, ties);
         // the first (slot, wave) pair whose running tie count reaches `need` holds the last
         // kept tie
         const int mine = lane < NP ? sh.cnt[lane] : 0;
         const uint64_t reach = ballot(lane < NP && excl + mine >= need);
         const int pstar = reach ? __builtin_ctzll(reach) : 0;
         const int before = __builtin_amdgcn_readlane(excl, pstar);
-        if (w == pstar % kTkWaves && lane == 0) {
-#pragma unroll
-            for (int j = 0; j < VPT; ++j) {
-                if (j == pstar / kTkWaves) sh.ilast = j * kTkThreads + w * 64 + nth_set_bit(tb[j], need - before);
-            }
-        }
-        if (tid == 0) sh.T = T;
         __syncthreads();
-    }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const uint64_t b = ballot(kv[j] == T);  // uniform control flow
+            if (j == pstar / kTkWaves && w == pstar % kTkWaves && lane == 0)
+                sh.ilast = j * kTkThreads + w * 64 + nth_set_bit(b, need - before);
+        }
+        __syncthreads();
+        const int ilast = sh.ilast;
 
-    // E. quantise the kept values with the chunk's absmax; error feedback for all
-    const uint32_t T = sh.T;
-    const int ilast = sh.ilast;
-    const float absmax = __uint_as_float(M);
-    const float step = absmax / (float)QMAX;
-    const float inv = (M != 0u) ? 1.0f / step : 0.0f;
-    uint64_t sb[VPT];
-    int qv[VPT];
+        // E'. count the kept elements per (slot, wave), then write every element's error
+        //     and compact the kept ones (their ballots are taken again, in uniform flow)
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int i = j * kTkThreads + tid;
-        const float h = __uint_as_float(kv[j] | ((sgn >> j) & 1u) << 31);
-        // keys above T are real elements; ties are kept up to index ilast (< len)
-        const bool sel = kv[j] > T || (kv[j] == T && i <= ilast);
-        const float rq = __builtin_amdgcn_fmed3f(__builtin_rintf(h * inv), (float)(-QMAX - 1), (float)QMAX);
-        const int q = (int)rq;
-        const float d = (float)q * step;
-        const float en = sel ? h - d : h;
-        if (FULL || i < len) p.e[base + i] = en;
-        sb[j] = ballot(sel);
-        qv[j] = q;
-        if (lane == 0) sh.cnt[j * kTkWaves + w] = __popcll(sb[j]);
-    }
-    __syncthreads();
-    int total = 0;
-    const int excl = pair_prefix<VPT>(sh, lane, total);
-    uint16_t* idx_out = p.idx + chunk * p.k;
+        for (int j = 0; j < VPT; ++j) {
+            const bool kept = kv[j] > T || (kv[j] == T && j * kTkThreads + tid <= ilast);
+            const int c = __popcll(ballot(kept));
+            if (lane == 0) sh.cnt[j * kTkWaves + w] = c;
+        }
+        __syncthreads();
+        int nkept = 0;
+        const int kex = pair_prefix<NP>(sh, lane, nkept);
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int bj = __builtin_amdgcn_readlane(excl, j * kTkWaves + w);  // uniform control flow
-        if ((sb[j] >> lane) & 1u) {
-            // pos < keff when the selection is right; the guard keeps a wrong selection from
-            // writing outside this chunk's slots
-            const int pos = bj + mbcnt(sb[j]);
-            if (pos < keff) {
-                idx_out[pos] = (uint16_t)(j * kTkThreads + tid);
-                sh.code[pos] = (uint8_t)((uint32_t)qv[j] & ((1u << BITS) - 1u));
+        for (int j = 0; j < VPT; ++j) {
+            const int i = j * kTkThreads + tid;
+            const bool kept = kv[j] > T || (kv[j] == T && i <= ilast);
+            const uint64_t b = ballot(kept);
+            const int bj = __builtin_amdgcn_readlane(kex, j * kTkWaves + w);  // uniform control flow
+            const float h = h_of(kv[j], sgn, j);
+            if (kept) {
+                // pos < keff when the selection is right; the guard keeps a wrong selection
+                // from writing outside this chunk's slots
+                const int pos = bj + mbcnt(b);
+                const int q = quantise<BITS>(h, inv);
+                p.e[base + i] = h - (float)q * step;
+                if (pos < keff) {
+                    idx_out[pos] = (uint16_t)i;
+                    sh.code[pos] = (uint8_t)((uint32_t)q & CMASK);
+                }
+            } else if (FULL || i < len) {
+                p.e[base + i] = h;
             }
         }
     }
@@ -290,26 +332,37 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
     if (tid == 0) p.absmax[chunk] = absmax;
 }
 
-// Grid-strides over chunks; the barrier at the end of each chunk lets the next one reuse
-// the LDS staging.
-template <int VPT, int BITS>
-__global__ __launch_bounds__(kTkThreads) void tk_kernel(TkParams p, int64_t nchunks) {
+// Grid-strides over chunks [c0, c1); the barrier at the end of each chunk lets the next
+// one reuse the LDS staging.  Full chunks and the short last chunk are separate kernels,
+// so the full-chunk code carries no bounds masks (registers are allocated per kernel).
+template <int VPT, int BITS, bool FULL>
+__global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(LOCO_TK_WAVES_PER_EU)))
+void tk_kernel(TkParams p, int64_t c0, int64_t c1) {
     __shared__ TkShared sh;
-    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        if ((c + 1) * (kTkThreads * VPT) <= p.n) tk_chunk<VPT, BITS, true>(p, c, sh);
-        else tk_chunk<VPT, BITS, false>(p, c, sh);
+    for (int64_t c = c0 + blockIdx.x; c < c1; c += gridDim.x) {
+        tk_chunk<VPT, BITS, FULL>(p, c, sh);
         __syncthreads();
     }
 }
 
-template <int BITS>
+template <int BITS, bool FULL>
 const void* pick_chunk(int chunk) {
     switch (chunk) {
-        case 256: return (const void*)&tk_kernel<1, BITS>;
-        case 512: return (const void*)&tk_kernel<2, BITS>;
-        case 1024: return (const void*)&tk_kernel<4, BITS>;
-        case 2048: return (const void*)&tk_kernel<8, BITS>;
-        case 4096: return (const void*)&tk_kernel<16, BITS>;
+        case 256: return (const void*)&tk_kernel<1, BITS, FULL>;
+        case 512: return (const void*)&tk_kernel<2, BITS, FULL>;
+        case 1024: return (const void*)&tk_kernel<4, BITS, FULL>;
+        case 2048: return (const void*)&tk_kernel<8, BITS, FULL>;
+        case 4096: return (const void*)&tk_kernel<16, BITS, FULL>;
+    }
+    return nullptr;
+}
+
+template <bool FULL>
+const void* pick(int chunk, int bits) {
+    switch (bits) {
+        case 2: return pick_chunk<2, FULL>(chunk);
+        case 4: return pick_chunk<4, FULL>(chunk);
+        case 8: return pick_chunk<8, FULL>(chunk);
     }
     return nullptr;
 }
@@ -317,17 +370,23 @@ const void* pick_chunk(int chunk) {
 }  // namespace
 
 hipError_t launch_tk(const TkParams& p, int chunk, int bits, hipStream_t stream) {
-    const void* k = nullptr;
-    switch (bits) {
-        case 2: k = pick_chunk<2>(chunk); break;
-        case 4: k = pick_chunk<4>(chunk); break;
-        case 8: k = pick_chunk<8>(chunk); break;
+    const void* kfull = pick<true>(chunk, bits);
+    const void* ktail = pick<false>(chunk, bits);
+    if (!kfull || !ktail) return hipErrorInvalidValue;
+    int64_t nfull = p.n / chunk;
+    int64_t nall = (p.n + chunk - 1) / chunk;
+    if (nfull > 0) {
+        int64_t c0 = 0;
+        const int64_t grid = nfull < kTkMaxGrid ? nfull : kTkMaxGrid;
+        void* args[] = {(void*)&p, (void*)&c0, (void*)&nfull};
+        const hipError_t st = hipLaunchKernel(kfull, dim3((unsigned)grid), dim3(kTkThreads), args, 0, stream);
+        if (st != hipSuccess) return st;
     }
-    if (!k) return hipErrorInvalidValue;
-    int64_t chunks = (p.n + chunk - 1) / chunk;
-    const int64_t grid = chunks < kTkMaxGrid ? chunks : kTkMaxGrid;
-    void* args[] = {(void*)&p, (void*)&chunks};
-    return hipLaunchKernel(k, dim3((unsigned)grid), dim3(kTkThreads), args, 0, stream);
+    if (nall > nfull) {
+        void* args[] = {(void*)&p, (void*)&nfull, (void*)&nall};
+        return hipLaunchKernel(ktail, dim3(1), dim3(kTkThreads), args, 0, stream);
+    }
+    return hipSuccess;
 }
 
 }  // namespace loco
