@@ -34,6 +34,60 @@ __device__ __forceinline__ int code_of(u32x2 w, int j) {
     else return __builtin_amdgcn_sbfe(w.x, j * BITS, BITS);
 }
 
+// v_cvt_f32_ubyteN: byte N of x as a float, in one instruction (the compiler otherwise
+// extracts the byte with a separate bit-field op first).
+template <int N>
+__device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
+    float r;
+    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ void acc_byte(float& a, uint32_t x, float step, float off) {
+    a = a + __builtin_fmaf(ubyte_to_f32<N>(x), step, off);
+}
+
+// acc[j] += fl(q_j * step) for the 8 codes held in w.  At 4 and 8 bits the codes are
+// biased to unsigned (q + 2^(b-1), one xor for all of them), converted with the byte
+// converts, and fl(q*step) is formed as fma(q + 2^(b-1), step, -2^(b-1)*step): the fma's
+// exact value is q*step, rounded once, so the result is bit-identical to rounding q*step
+// (2^(b-1)*step is exact).  2-bit codes use a sign-extending bit-field extract.
+template <int BITS>
+__device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float step) {
+    if constexpr (BITS == 4) {
+        const uint32_t x = w.x ^ 0x88888888u;
+        const uint32_t lo = x & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
+        const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+        const float off = -8.0f * step;
+        acc_byte<0>(acc[0], lo, step, off);
+        acc_byte<0>(acc[1], hi, step, off);
+        acc_byte<1>(acc[2], lo, step, off);
+        acc_byte<1>(acc[3], hi, step, off);
+        acc_byte<2>(acc[4], lo, step, off);
+        acc_byte<2>(acc[5], hi, step, off);
+        acc_byte<3>(acc[6], lo, step, off);
+        acc_byte<3>(acc[7], hi, step, off);
+    } else if constexpr (BITS == 8) {
+        const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
+        const float off = -128.0f * step;
+        acc_byte<0>(acc[0], x0, step, off);
+        acc_byte<1>(acc[1], x0, step, off);
+        acc_byte<2>(acc[2], x0, step, off);
+        acc_byte<3>(acc[3], x0, step, off);
+        acc_byte<0>(acc[4], x1, step, off);
+        acc_byte<1>(acc[5], x1, step, off);
+        acc_byte<2>(acc[6], x1, step, off);
+        acc_byte<3>(acc[7], x1, step, off);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kDrVec; ++j) acc[j] = acc[j] + (float)code_of<BITS>(w, j) * step;
+    }
+}
+
 template <int BITS, int B, bool FIXED>
 __device__ __forceinline__ float peer_step(const DrPeerDev& pe, int64_t i0, float fixed_step) {
     constexpr int QMAX = (1 << (BITS - 1)) - 1;
@@ -61,6 +115,7 @@ __device__ __forceinline__ void store_out8(void* out, int64_t i0, const float (&
 
 template <int BITS, int B, bool FIXED, bool OBF>
 __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
+    static_assert(kDrTile % B == 0, "a wave tile spans whole scale blocks");
     constexpr int SUB = 64 * kDrVec;
     const int lane = lane_id();
     const int64_t nwaves = (int64_t)gridDim.x * (kDrThreads / kWave);
@@ -75,22 +130,58 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
             for (int j = 0; j < kDrVec; ++j) acc[u][j] = 0.0f;
 
         if ((t + 1) * kDrTile <= p.n) {
-            // whole wave tile in range
-#pragma unroll 2
-            for (int pi = 0; pi < p.npeers; ++pi) {
-                const DrPeerDev pe = p.peer[pi];
-                u32x2 w[kDrUnroll];
-                float step[kDrUnroll];
+            // whole wave tile in range.  The tile spans BPT scale blocks; the steps of G
+            // peers x BPT blocks are computed one per lane (one division per lane per G
+            // peers) and each lane fetches its block's step with a lane shuffle.
+            constexpr int BPT = kDrTile / B;
+            constexpr int G = 64 / BPT;
+            const int64_t blk0 = t * (kDrTile / B);
+            int myblk[kDrUnroll];
 #pragma unroll
-                for (int u = 0; u < kDrUnroll; ++u) {
-                    w[u] = load_codes8<BITS>(pe.codes, base + u * SUB);
-                    step[u] = peer_step<BITS, B, FIXED>(pe, base + u * SUB, p.fixed_step);
+            for (int u = 0; u < kDrUnroll; ++u) myblk[u] = (int)((base + u * SUB) / B - blk0);
+            for (int pg = 0; pg < p.npeers; pg += G) {
+                const int ng = p.npeers - pg < G ? p.npeers - pg : G;
+                // codes of a batch of peers, all loads in flight together (slots past the
+                // group re-read its last peer and are not accumulated)
+                u32x2 w[kDrPeerBatch][kDrUnroll];
+                auto load_batch = [&](int q0) {
+#pragma unroll
+                    for (int b = 0; b < kDrPeerBatch; ++b) {
+                        const int q = q0 + b < ng ? q0 + b : ng - 1;
+                        const uint8_t* codes = p.peer[pg + q].codes;
+#pragma unroll
+                        for (int u = 0; u < kDrUnroll; ++u) w[b][u] = load_codes8<BITS>(codes, base + u * SUB);
+                    }
+                };
+                load_batch(0);  // issued before the scales, so both latencies overlap
+                float stp = p.fixed_step;
+                if constexpr (!FIXED) {
+                    constexpr int QMAX = (1 << (BITS - 1)) - 1;
+                    // every lane loads its block's absmax of each peer of the group and keeps
+                    // the one of its own peer: one division per lane per group
+                    float am = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < G; ++q) {
+                        const int qq = q < ng ? q : ng - 1;
+                        const float v = p.peer[pg + qq].absmax[blk0 + lane % BPT];
+                        am = (lane / BPT == q) ? v : am;
+                    }
+                    stp = am / (float)QMAX;  // 0 for an all-zero block
                 }
+                for (int q0 = 0; q0 < ng; q0 += kDrPeerBatch) {
+                    if (q0 > 0) load_batch(q0);
+                    // accumulate in peer order
 #pragma unroll
-                for (int u = 0; u < kDrUnroll; ++u)
+                    for (int b = 0; b < kDrPeerBatch; ++b) {
+                        if (q0 + b < ng) {
 #pragma unroll
-                    for (int j = 0; j < kDrVec; ++j)
-                        acc[u][j] = acc[u][j] + (float)code_of<BITS>(w[u], j) * step[u];
+                            for (int u = 0; u < kDrUnroll; ++u) {
+                                const float step = FIXED ? stp : __shfl(stp, (q0 + b) * BPT + myblk[u], 64);
+                                accumulate8<BITS>(acc[u], w[b][u], step);
+                            }
+                        }
+                    }
+                }
             }
 #pragma unroll
             for (int u = 0; u < kDrUnroll; ++u) store_out8<OBF>(p.out, base + u * SUB, acc[u], p.out_scale);

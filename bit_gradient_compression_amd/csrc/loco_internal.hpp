@@ -78,6 +78,7 @@ constexpr int kDrVec = 8;                          // consecutive outputs per la
 constexpr int kDrUnroll = LOCO_DR_UNROLL;          // sub-tiles per wave tile
 constexpr int kDrTile = 64 * kDrVec * kDrUnroll;   // elements per wave tile
 constexpr int kDrThreads = LOCO_DR_THREADS;
+constexpr int kDrPeerBatch = 8;                    // peers whose codes are loaded together
 
 struct DrPeerDev {
     const uint8_t* codes;
