@@ -30,7 +30,7 @@ namespace loco {
 #define LOCO_CQ_XCD_RUN 32
 #endif
 #ifndef LOCO_DR_XCD_RUN
-#define LOCO_DR_XCD_RUN 1
+#define LOCO_DR_XCD_RUN 16
 #endif
 constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 // Workgroups are dispatched round-robin over the chip's 8 XCDs (each with its own L2).

@@ -17,6 +17,8 @@ extracted text, so each step below is rebuilt from the prose around the equation
       decompressed low-bit version.
     - Sec. 3.2, Eqn. (5): the error is a beta-weighted moving average of the
       historical compression errors, starting from zero.
+    - Sec. 3.2, Eqn. (7): the error is kept as 8-bit codes of a fixed scale s_e
+      (the compressor of Eqn. (1) with 8 bits), and reset to zero every T_c steps.
     - Sec. 3.3, Eqn. (8): the synchronised gradient is the average over the N nodes
       of the decompressed low-bit gradients, computed in high precision; with FSDP
       each node averages only its own partition (all2all, then a local average).
@@ -47,7 +49,8 @@ import numpy as np
 __all__ = [
     "bf16_rne", "bf16_to_f32", "widen", "qmax_of",
     "compensate", "absmax_quantize", "fixed_scale_quantize", "dequantize",
-    "error_update", "pack_codes", "unpack_codes", "compensate_quantize",
+    "error_update", "error_decompress", "error_compress", "pack_codes", "unpack_codes",
+    "compensate_quantize",
     "cq_algorithmic_bytes", "block_steps", "dequant_reduce", "dr_algorithmic_bytes",
     "topk_order_select", "topk_quantize", "tk_algorithmic_bytes",
 ]
@@ -201,13 +204,28 @@ def _absmax_compressor(bits, block, fixed_scale):
     return comp
 
 
+def error_decompress(e8: np.ndarray, s_e: float, ftype=np.float32) -> np.ndarray:
+    """The 8-bit error as a float (LoCo Sec. 3.1, Eqn. (2)): e8 * fl(1 / s_e), the
+    decompressor of Eqn. (1) with the error's own scale."""
+    return np.asarray(e8, dtype=np.int8).astype(ftype) * (ftype(1) / ftype(s_e))
+
+
+def error_compress(e_tilde: np.ndarray, s_e: float) -> np.ndarray:
+    """LoCo Sec. 3.2, Eqn. (7): compressor(e~; s_e, 8) = Round_8(s_e * e~), nearest
+    integer (ties to even) inside [-128, 127]."""
+    ft = e_tilde.dtype.type
+    return np.clip(np.rint(e_tilde * ft(s_e)), -128, 127).astype(np.int8)
+
+
 def compensate_quantize(g, e, *, bits, block, beta, fixed_scale=0.0,
                         grad_dtype="f32", err_dtype="f32", ftype=np.float32,
-                        compressor=None):
-    """One LoCo step on one segment (LoCo Sec. 3.1 - 3.2, Eqns. (2) - (5)).
+                        compressor=None, err_scale=0.0, reset=False):
+    """One LoCo step on one segment (LoCo Sec. 3.1 - 3.2, Eqns. (2) - (5), (7)).
 
-    g, e: stored gradient and error (float32 arrays, or uint16 bf16 patterns when
-    the dtype says 'bf16').  Returns a dict with
+    g, e: stored gradient and error (float32 arrays, uint16 bf16 patterns when the dtype
+    says 'bf16', int8 codes of the paper's 8-bit error when err_dtype is 'i8', whose
+    scale s_e is `err_scale`).  `reset` is the periodic reset of Eqn. (7): this step
+    stores e = 0.  Returns a dict with
       codes   packed payload bytes (ceil(n*bits/8))       [compressor output]
       absmax  float per block (None in fixed-scale mode)
       e_new   the updated error in its storage format
@@ -217,14 +235,23 @@ def compensate_quantize(g, e, *, bits, block, beta, fixed_scale=0.0,
     identity-compressor check.
     """
     gf = widen(g, grad_dtype, ftype)
-    ef = widen(e, err_dtype, ftype)
+    if err_dtype == "i8":
+        if not err_scale > 0:
+            raise ValueError("an 8-bit error needs its scale s_e > 0")
+        ef = error_decompress(e, err_scale, ftype)
+    else:
+        ef = widen(e, err_dtype, ftype)
     h = compensate(gf, ef)
     comp = compressor or _absmax_compressor(bits, block, fixed_scale)
     d, info = comp(h)
     r = h - d
     e_new = error_update(ef, r, beta)
+    if reset:
+        e_new = np.zeros_like(e_new)
     if err_dtype == "bf16":
         e_store = bf16_rne(e_new.astype(np.float32))
+    elif err_dtype == "i8":
+        e_store = error_compress(e_new, err_scale)
     else:
         e_store = e_new.astype(ftype)
     out = {"d": d, "e_new": e_store, "q": info.get("q"), "absmax": info.get("absmax")}

@@ -41,11 +41,15 @@ def _cases(name):
 
 def cq_cases():
     for c in _cases("cq_worked.txt"):
+        ed = c.get("err_dtype", ["f32"])[0]
+        et = np.int8 if ed == "i8" else np.float32
         yield {"bits": int(c["bits"][0]), "block": int(c["block"][0]), "beta": float(c["beta"][0]),
-               "g": np.array(c["g"], np.float32), "e": np.array(c["e"], np.float32),
+               "err_dtype": ed, "err_scale": float(c.get("err_scale", ["0"])[0]),
+               "reset": bool(int(c.get("reset", ["0"])[0])),
+               "g": np.array(c["g"], np.float32), "e": np.array(c["e"], np.float64).astype(et),
                "absmax": np.array(c["absmax"], np.float32),
                "codes": bytes.fromhex("".join(c["codes"])),
-               "e_new": np.array(c["e_new"], np.float32)}
+               "e_new": np.array(c["e_new"], np.float64).astype(et)}
 
 
 def dr_case():

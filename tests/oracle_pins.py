@@ -230,7 +230,8 @@ def pin_pack_layout(O):
 
 def pin_cq_worked(O):
     for c in golden_io.cq_cases():
-        out = O.compensate_quantize(c["g"], c["e"], bits=c["bits"], block=c["block"], beta=c["beta"])
+        out = O.compensate_quantize(c["g"], c["e"], bits=c["bits"], block=c["block"], beta=c["beta"],
+                                    err_dtype=c["err_dtype"], err_scale=c["err_scale"], reset=c["reset"])
         assert np.array_equal(out["absmax"], c["absmax"]), ("absmax", out["absmax"], c["absmax"])
         assert out["codes"].tobytes() == c["codes"], ("codes", out["codes"].tobytes().hex())
         assert np.array_equal(out["e_new"], c["e_new"]), ("e_new", out["e_new"], c["e_new"])
@@ -344,9 +345,85 @@ def pin_topk_error_feedback(O):
     assert np.max(np.abs(sent - (gsum - e))) <= 1e-12 * K
 
 
+# -- the paper's 8-bit error (LoCo Sec. 3.2, Eqn. (7)) ------------------------------------------
+
+def pin_i8_error_accounting(O):
+    """With the error stored as e8 (value E = e8/s_e), g_k - d_k = (E_k - delta_k - E_{k-1}) /
+    (1 - beta), delta_k = E_k - e~_k the 8-bit rounding of the new error; so the sum over K
+    steps is (E_K - E_0)/(1 - beta) within K / (2 s_e (1 - beta)) when nothing clips
+    (float64 twin)."""
+    rng = _rng(21)
+    n, beta, K, s_e = 4096, 0.9, 40, 2.0 ** 18
+    e8 = np.zeros(n, np.int8)
+    acc = np.zeros(n)
+    for _ in range(K):
+        g = (rng.standard_normal(n) * 1e-3).astype(F32).astype(np.float64)
+        out = O.compensate_quantize(g, e8, bits=4, block=128, beta=beta, grad_dtype="f64",
+                                    err_dtype="i8", err_scale=s_e, ftype=np.float64)
+        acc += g - out["d"]
+        e8 = out["e_new"]
+        assert e8.max() < 127 and e8.min() > -128, "clipped: the bound below needs no clipping"
+    E_K = e8.astype(np.float64) / s_e
+    slack = K / (2 * s_e * (1 - beta)) * (1 + 1e-9)
+    dev = np.abs(acc - E_K / (1 - beta))
+    assert np.all(dev <= slack), (dev.max(), slack)
+    assert dev.max() > slack * 1e-3  # the 8-bit rounding is really there
+
+
+def pin_i8_equals_float_when_exact(O):
+    """When every new error is a multiple of 1/s_e inside the 8-bit range, storing it as
+    e8 loses nothing: the chain equals the fp32-error chain bitwise.  Built with a fixed
+    scale s = 4, beta = 1/2 and g on the grid 1/64, so e~ lies on the grid 1/128."""
+    rng = _rng(22)
+    n, s_e = 3000, 128.0
+    e_f = np.zeros(n, F32)
+    e8 = np.zeros(n, np.int8)
+    for _ in range(12):
+        g = (rng.integers(-20, 21, n) / 64.0).astype(F32)
+        a = O.compensate_quantize(g, e_f, bits=4, block=64, beta=0.5, fixed_scale=4.0)
+        b = O.compensate_quantize(g, e8, bits=4, block=64, beta=0.5, fixed_scale=4.0,
+                                  err_dtype="i8", err_scale=s_e)
+        assert np.array_equal(a["codes"], b["codes"])
+        assert np.array_equal(a["d"], b["d"])
+        assert np.all(np.abs(a["e_new"] * s_e) <= 127)
+        assert np.array_equal(a["e_new"], b["e_new"].astype(F32) / F32(s_e))
+        e_f, e8 = a["e_new"], b["e_new"]
+
+
+def pin_reset(O):
+    """The periodic reset of Eqn. (7): the step's codes are unchanged, its stored error is
+    zero, and the next step starts from e = 0."""
+    rng = _rng(23)
+    n = 2000
+    for ed, e0 in (("f32", (rng.standard_normal(n) * 1e-4).astype(F32)),
+                   ("i8", rng.integers(-100, 100, n).astype(np.int8))):
+        kw = dict(bits=4, block=128, beta=0.9, err_dtype=ed, err_scale=2.0 ** 17)
+        g = (rng.standard_normal(n) * 1e-3).astype(F32)
+        a = O.compensate_quantize(g, e0, **kw)
+        b = O.compensate_quantize(g, e0, reset=True, **kw)
+        assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["absmax"], b["absmax"])
+        assert not np.any(b["e_new"])
+        c = O.compensate_quantize(g, b["e_new"], **kw)
+        d0 = O.compensate_quantize(g, np.zeros_like(e0), **kw)
+        assert np.array_equal(c["codes"], d0["codes"])
+
+
+def pin_i8_compressor_vs_torch(O):
+    """The error's compressor Round_8(s_e * e~) equals PyTorch's qint8 quantiser with scale
+    1/s_e (a power of two, so its reciprocal is s_e exactly), ties and clamps included."""
+    rng = _rng(24)
+    for s_e in (2.0 ** 10, 2.0 ** 17, 2.0 ** 21):
+        x = (rng.standard_normal(20000) * 60 / s_e).astype(F32)
+        x[:200] = (rng.integers(-140, 140, 200) + 0.5).astype(F32) / F32(s_e)  # exact ties, clamps
+        want = torch.quantize_per_tensor(torch.from_numpy(x), 1.0 / s_e, 0, torch.qint8).int_repr().numpy()
+        assert np.array_equal(O.error_compress(x, s_e), want)
+        assert np.array_equal(O.error_decompress(want, s_e), want.astype(F32) / F32(s_e))
+
+
 ALL_PINS = [
     pin_identity_compressor, pin_beta_zero_is_efc, pin_quantisation_bound,
     pin_random_walk_bounded, pin_telescoping, pin_fixed_scale_golden, pin_torch_quantiser,
     pin_topk_brute_force, pin_pack_layout, pin_cq_worked, pin_dr_worked, pin_topk_worked,
     pin_dequant_reduce, pin_zero_blocks, pin_bf16_rne, pin_topk_error_feedback,
+    pin_i8_error_accounting, pin_i8_equals_float_when_exact, pin_reset, pin_i8_compressor_vs_torch,
 ]

@@ -104,6 +104,20 @@ def _steps_no_qmax(absmax, bits):
     return np.asarray(absmax).copy()
 
 
+def _edecomp_times_scale(e8, s_e, ftype=np.float32):
+    return np.asarray(e8, dtype=np.int8).astype(ftype) * ftype(s_e)
+
+
+def _ecomp_floor(e_tilde, s_e):
+    ft = e_tilde.dtype.type
+    return np.clip(np.floor(e_tilde * ft(s_e)), -128, 127).astype(np.int8)
+
+
+def _ecomp_no_clamp(e_tilde, s_e):
+    ft = e_tilde.dtype.type
+    return np.rint(e_tilde * ft(s_e)).astype(np.int64).astype(np.int8)
+
+
 MUTATIONS = {
     "error_update drops beta*e": ("error_update", _drop_beta_term),
     "error_update swaps beta and 1-beta": ("error_update", _swap_weights),
@@ -119,6 +133,9 @@ MUTATIONS = {
     "no sign extension": ("unpack_codes", _unpack_unsigned),
     "bf16 truncation": ("bf16_rne", _bf16_truncate),
     "decoder step without /qmax": ("block_steps", _steps_no_qmax),
+    "8-bit error decompressed with s_e, not 1/s_e": ("error_decompress", _edecomp_times_scale),
+    "8-bit error compressed with floor": ("error_compress", _ecomp_floor),
+    "8-bit error compressed without clamp": ("error_compress", _ecomp_no_clamp),
 }
 
 
