@@ -6,8 +6,9 @@ A step is one pass of the rank's path on the 7B FSDP-shard workload:
   destination, blocks restarting per partition), then
   dequant-reduce of the 8 peer payloads of the rank's own partition into bf16 (x 1/8).
 Inputs are resident in HBM before the timed region; the error buffer carries over from
-step to step.  The SparseLoCo-style Top-k mode (2^28 fp32, chunk 4096, k = 82, 2-bit)
-and the 8-bit variant are timed in the same run and reported under "modes".
+step to step.  The SparseLoCo-style Top-k mode (2^28 fp32, chunk 4096, k = 82, 2-bit),
+the 8-bit-code variant and the 8-bit-error variant (LoCo Eqn. (7)) are timed in the same
+run and reported under "modes".
 
 Prints one JSON line.  value = gradient GB/s = 842,000,000 x 2 bytes / step time.
 roofline: the compensate-quantize kernel's algorithmic bytes / its average launch time
@@ -235,6 +236,19 @@ def main():
                                                       "frac_hbm": round(b8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                                       "grad_GBps": round(n * 2 / ms / 1e6, 1)}
         del codes8, e8, segs8
+        # the paper's 8-bit error (LoCo Eqn. (7), s_e = 2^17) with 4-bit codes, same shard
+        ei8 = torch.zeros(n, dtype=torch.int8, device=dev)
+        segs_i8 = [(g[i * part:(i + 1) * part], ei8[i * part:(i + 1) * part], *segs[i][2:]) for i in range(PARTS)]
+        ms = timed(lambda: loco.loco_compensate_quantize_ex(segs_i8, bits=BITS, block=BLOCK, beta=BETA,
+                                                            err_scale=2.0 ** 17, stream=stream),
+                   stream, max(3, args.steps // 3))
+        bi8 = cq_bytes(sizes, 2, 1, BITS, BLOCK)
+        modes["compensate_quantize_4bit_i8err_7b_shard"] = {"avg_ms": round(ms, 4), "alg_bytes": bi8,
+                                                            "GBps": round(bi8 / ms / 1e6, 1),
+                                                            "frac_hbm": round(bi8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                                            "grad_GBps": round(n * 2 / ms / 1e6, 1),
+                                                            "err_scale": 2.0 ** 17}
+        del ei8, segs_i8
         # SparseLoCo-style mode on its own workload
         nt = W.SPARSE_N
         gt = W.sparseloco_grad(0, n=nt, device=dev)

@@ -19,7 +19,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool bits_ok(int bits) { return bits == 2 || bits == 4 || bits == 8; }
 bool block_ok(int block) { return block == 64 || block == 128 || block == 256 || block == 512; }
 bool dtype_ok(int d) { return d == LOCO_F32 || d == LOCO_BF16; }
-int dtype_size(int d) { return d == LOCO_BF16 ? 2 : 4; }
+int dtype_size(int d) { return d == LOCO_I8 ? 1 : (d == LOCO_BF16 ? 2 : 4); }
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -39,7 +39,7 @@ constexpr int64_t kMaxElems = (int64_t)1 << 52;
 
 using namespace loco;
 
-LOCO_API int loco_version(void) { return 10000; }
+LOCO_API int loco_version(void) { return 10100; }
 
 LOCO_API const char* loco_status_string(int status) {
     switch (status) {
@@ -52,17 +52,27 @@ LOCO_API const char* loco_status_string(int status) {
     return "unknown status";
 }
 
-LOCO_API int loco_compensate_quantize(const loco_cq_segment_t* segs, int nseg,
-                                      loco_dtype_t grad_dtype, loco_dtype_t err_dtype,
-                                      int bits, int block, float beta, float fixed_scale,
-                                      void* stream) {
+namespace {
+
+// Shared body of both compensate-quantize entry points.
+int compensate_quantize(const loco_cq_segment_t* segs, int nseg, int grad_dtype, int err_dtype,
+                        const loco_cq_options_t& o, hipStream_t st) {
     if (nseg < 0 || (nseg > 0 && !segs)) return LOCO_ERR_INVALID;
-    if (!dtype_ok(grad_dtype) || !dtype_ok(err_dtype)) return LOCO_ERR_INVALID;
+    if (!dtype_ok(grad_dtype)) return LOCO_ERR_INVALID;
+    if (!dtype_ok(err_dtype) && err_dtype != LOCO_I8) return LOCO_ERR_INVALID;
+    const int bits = o.bits, block = o.block;
     if (bits < 1 || bits > 8) return LOCO_ERR_INVALID;
     if (!bits_ok(bits)) return LOCO_ERR_UNSUPPORTED;
-    if (!isfinite(beta) || beta < 0.0f || beta > 1.0f) return LOCO_ERR_INVALID;
-    if (!isfinite(fixed_scale) || fixed_scale < 0.0f) return LOCO_ERR_INVALID;
-    const bool fixed = fixed_scale > 0.0f;
+    if (!isfinite(o.beta) || o.beta < 0.0f || o.beta > 1.0f) return LOCO_ERR_INVALID;
+    if (!isfinite(o.fixed_scale) || o.fixed_scale < 0.0f) return LOCO_ERR_INVALID;
+    float err_step = 0.0f;
+    if (err_dtype == LOCO_I8) {
+        // s_e > 0 and 256/s_e finite: the decode e8*fl(1/s_e) and its biased form stay finite.
+        if (!isfinite(o.err_scale) || !(o.err_scale > 0.0f)) return LOCO_ERR_INVALID;
+        err_step = 1.0f / o.err_scale;
+        if (!isfinite(256.0f * err_step)) return LOCO_ERR_INVALID;
+    }
+    const bool fixed = o.fixed_scale > 0.0f;
     if (!fixed) {
         if (block <= 0) return LOCO_ERR_INVALID;
         if (!block_ok(block)) return LOCO_ERR_UNSUPPORTED;
@@ -88,13 +98,18 @@ LOCO_API int loco_compensate_quantize(const loco_cq_segment_t* segs, int nseg,
 
     CqParams p;
     memset(&p, 0, sizeof(p));
-    p.beta = beta;
-    p.omega = 1.0f - beta;
+    p.beta = o.beta;
+    p.omega = 1.0f - o.beta;
     if (fixed) {
-        p.fixed_inv = fixed_scale;
-        p.fixed_step = 1.0f / fixed_scale;
+        p.fixed_inv = o.fixed_scale;
+        p.fixed_step = 1.0f / o.fixed_scale;
     }
-    hipStream_t st = (hipStream_t)stream;
+    if (err_dtype == LOCO_I8) {
+        p.err_scale = o.err_scale;
+        p.err_step = err_step;
+    }
+    p.reset = o.reset_error != 0;
+    const int64_t tile = cq_tile_elems(err_dtype);
     int i = 0;
     while (i < nseg) {
         p.nseg = 0;
@@ -109,13 +124,35 @@ LOCO_API int loco_compensate_quantize(const loco_cq_segment_t* segs, int nseg,
             d.absmax = s.absmax;
             d.n = s.n;
             d.tile0 = p.ntiles;
-            p.ntiles += (s.n + kCqTile - 1) / kCqTile;
+            p.ntiles += (s.n + tile - 1) / tile;
         }
         if (p.nseg == 0) break;
-        if (launch_cq(p, grad_dtype == LOCO_BF16, err_dtype == LOCO_BF16, bits, block, fixed, st) != hipSuccess)
-            return LOCO_ERR_HIP;
+        if (launch_cq(p, grad_dtype, err_dtype, bits, block, fixed, st) != hipSuccess) return LOCO_ERR_HIP;
     }
     return LOCO_OK;
+}
+
+}  // namespace
+
+LOCO_API int loco_compensate_quantize(const loco_cq_segment_t* segs, int nseg,
+                                      loco_dtype_t grad_dtype, loco_dtype_t err_dtype,
+                                      int bits, int block, float beta, float fixed_scale,
+                                      void* stream) {
+    if (err_dtype == LOCO_I8) return LOCO_ERR_INVALID;  // needs s_e: use the _ex entry point
+    loco_cq_options_t o;
+    memset(&o, 0, sizeof(o));
+    o.bits = bits;
+    o.block = block;
+    o.beta = beta;
+    o.fixed_scale = fixed_scale;
+    return compensate_quantize(segs, nseg, grad_dtype, err_dtype, o, (hipStream_t)stream);
+}
+
+LOCO_API int loco_compensate_quantize_ex(const loco_cq_segment_t* segs, int nseg,
+                                         loco_dtype_t grad_dtype, loco_dtype_t err_dtype,
+                                         const loco_cq_options_t* opt, void* stream) {
+    if (!opt) return LOCO_ERR_INVALID;
+    return compensate_quantize(segs, nseg, grad_dtype, err_dtype, *opt, (hipStream_t)stream);
 }
 
 LOCO_API int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_t n, int bits,

@@ -4,6 +4,9 @@
 // Sec. 3.1 Eqns. (1)-(3) and Sec. 3.2 Eqns. (4)-(5), with a per-block absmax scale:
 //   h = g + e;  absmax = max|h| per block;  step = absmax/qmax;  inv = 1/step
 //   q = clamp(rint(h*inv));  r = h - q*step;  e' = beta*e + (1-beta)*r
+// The error is stored as fp32, bf16, or the paper's 8-bit codes of a fixed scale s_e
+// (Sec. 3.2, Eqn. (7): e = e8 * fl(1/s_e) on load, e8' = clamp(rint(e' * s_e)) on store),
+// and a step may store e' = 0 instead (the periodic reset of Eqn. (7)).
 //
 // Mapping: a wavefront owns a tile of kCqUnroll sub-tiles of 512 elements; lane l owns
 // 8 consecutive elements of each sub-tile, so one bf16 gradient load, two fp32 error
@@ -21,57 +24,71 @@
 namespace loco {
 namespace {
 
-template <bool BF>
-__device__ __forceinline__ float load1(const void* p, int64_t i) {
-    if constexpr (BF) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+// Element kinds of the gradient (F32, BF16) and of the error (F32, BF16, I8).
+enum : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+
+template <int K>
+__device__ __forceinline__ float load1(const void* p, int64_t i, float estep) {
+    if constexpr (K == kBF16) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+    else if constexpr (K == kI8) return (float)((const int8_t*)p)[i] * estep;
     else return ((const float*)p)[i];
 }
 
-template <bool BF>
-__device__ __forceinline__ void store1(void* p, int64_t i, float v) {
-    if constexpr (BF) ((uint16_t*)p)[i] = bf16_rne(v);
+template <int K>
+__device__ __forceinline__ void store1(void* p, int64_t i, float v, float escale) {
+    if constexpr (K == kBF16) ((uint16_t*)p)[i] = bf16_rne(v);
+    else if constexpr (K == kI8) ((int8_t*)p)[i] = (int8_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(v * escale), -128.0f, 127.0f);
     else ((float*)p)[i] = v;
 }
 
-// 8 consecutive elements starting at i0 (16-byte aligned).  The gradient is read once:
-// non-temporal.
-template <bool BF>
-__device__ __forceinline__ void load8_nt(const void* p, int64_t i0, float (&x)[8]) {
-    if constexpr (BF) {
-        u32x4 w = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)p + i0));
+// 4 int8 codes (one word, biased by 0x80) -> e8 * estep, as fma(e8 + 128, estep,
+// -128 * estep): its exact value is e8 * estep, rounded once, the same as the product.
+__device__ __forceinline__ void i8x4_to_f32(uint32_t w, float estep, float off, float* x) {
+    const uint32_t u = w ^ 0x80808080u;
+    x[0] = __builtin_fmaf(ubyte_to_f32<0>(u), estep, off);
+    x[1] = __builtin_fmaf(ubyte_to_f32<1>(u), estep, off);
+    x[2] = __builtin_fmaf(ubyte_to_f32<2>(u), estep, off);
+    x[3] = __builtin_fmaf(ubyte_to_f32<3>(u), estep, off);
+}
+
+// 8 consecutive elements starting at i0 (16-byte aligned for 2- and 4-byte kinds, 8-byte
+// for int8).  NT: non-temporal (the gradient is read once).
+template <int K, bool NT>
+__device__ __forceinline__ void load8(const void* p, int64_t i0, float (&x)[8], float estep) {
+    if constexpr (K == kBF16) {
+        const u32x4* q = (const u32x4*)((const uint16_t*)p + i0);
+        const u32x4 w = NT ? __builtin_nontemporal_load(q) : *q;
         x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
         x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    } else if constexpr (K == kI8) {
+        const u32x2* q = (const u32x2*)((const int8_t*)p + i0);
+        const u32x2 w = NT ? __builtin_nontemporal_load(q) : *q;
+        const float off = -128.0f * estep;
+        i8x4_to_f32(w.x, estep, off, x);
+        i8x4_to_f32(w.y, estep, off, x + 4);
     } else {
         const f32x4* q = (const f32x4*)((const float*)p + i0);
-        f32x4 a = __builtin_nontemporal_load(q);
-        f32x4 b = __builtin_nontemporal_load(q + 1);
+        const f32x4 a = NT ? __builtin_nontemporal_load(q) : q[0];
+        const f32x4 b = NT ? __builtin_nontemporal_load(q + 1) : q[1];
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
         x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     }
 }
 
-template <bool BF>
-__device__ __forceinline__ void load8(const void* p, int64_t i0, float (&x)[8]) {
-    if constexpr (BF) {
-        u32x4 w = *(const u32x4*)((const uint16_t*)p + i0);
-        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-    } else {
-        const f32x4* q = (const f32x4*)((const float*)p + i0);
-        f32x4 a = q[0];
-        f32x4 b = q[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
-}
-
-template <bool BF>
-__device__ __forceinline__ void store8(void* p, int64_t i0, const float (&x)[8]) {
-    if constexpr (BF) {
+template <int K>
+__device__ __forceinline__ void store8(void* p, int64_t i0, const float (&x)[8], float escale) {
+    if constexpr (K == kBF16) {
         u32x4 w;
         w.x = bf16x2_rne(x[0], x[1]); w.y = bf16x2_rne(x[2], x[3]);
         w.z = bf16x2_rne(x[4], x[5]); w.w = bf16x2_rne(x[6], x[7]);
         __builtin_nontemporal_store(w, (u32x4*)((uint16_t*)p + i0));
+    } else if constexpr (K == kI8) {
+        uint32_t b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            b[j] = (uint32_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(x[j] * escale), -128.0f, 127.0f) & 0xFFu;
+        const u32x2 w = {b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24};
+        __builtin_nontemporal_store(w, (u32x2*)((int8_t*)p + i0));
     } else {
         f32x4* q = (f32x4*)((float*)p + i0);
         f32x4 a = {x[0], x[1], x[2], x[3]};
@@ -81,29 +98,30 @@ __device__ __forceinline__ void store8(void* p, int64_t i0, const float (&x)[8])
     }
 }
 
-template <bool GBF, bool EBF, int BITS, int B, bool FIXED, bool FULL>
+template <int GK, int EK, int BITS, int B, bool FIXED, bool FULL>
 __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int lane,
                                         const CqParams& p) {
     constexpr int QMAX = (1 << (BITS - 1)) - 1;
     constexpr int LPB = B / kCqVec;  // lanes per scale block
     constexpr int SUB = 64 * kCqVec;
-    float h[kCqUnroll][kCqVec];
-    float e[kCqUnroll][kCqVec];
+    constexpr int U = cq_unroll(EK);
+    float h[U][kCqVec];
+    float e[U][kCqVec];
 
     // Issue every load of the tile first.
 #pragma unroll
-    for (int u = 0; u < kCqUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int64_t i0 = base + u * SUB + lane * kCqVec;
         float g[kCqVec];
         if constexpr (FULL) {
-            load8_nt<GBF>(sg.g, i0, g);
-            load8<EBF>(sg.e, i0, e[u]);
+            load8<GK, true>(sg.g, i0, g, 0.0f);
+            load8<EK, false>(sg.e, i0, e[u], p.err_step);
         } else {
 #pragma unroll
             for (int j = 0; j < kCqVec; ++j) {
                 const bool ok = i0 + j < sg.n;
-                g[j] = ok ? load1<GBF>(sg.g, i0 + j) : 0.0f;
-                e[u][j] = ok ? load1<EBF>(sg.e, i0 + j) : 0.0f;
+                g[j] = ok ? load1<GK>(sg.g, i0 + j, 0.0f) : 0.0f;
+                e[u][j] = ok ? load1<EK>(sg.e, i0 + j, p.err_step) : 0.0f;
             }
         }
 #pragma unroll
@@ -111,7 +129,7 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
     }
 
 #pragma unroll
-    for (int u = 0; u < kCqUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int64_t i0 = base + u * SUB + lane * kCqVec;
         float step, inv, am = 0.0f;
         if constexpr (FIXED) {
@@ -145,9 +163,13 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
                 packed_lo |= f << (BITS * j);
             }
         }
+        if (p.reset) {  // Eqn. (7): this step stores a zero error
+#pragma unroll
+            for (int j = 0; j < kCqVec; ++j) en[j] = 0.0f;
+        }
 
         if constexpr (FULL) {
-            store8<EBF>(sg.e, i0, en);
+            store8<EK>(sg.e, i0, en, p.err_scale);
             uint8_t* c = sg.codes + (i0 * BITS) / 8;
             if constexpr (BITS == 8) {
                 u32x2 w = {packed_lo, packed_hi};
@@ -165,7 +187,7 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
             const int nvalid = left <= 0 ? 0 : (left >= kCqVec ? kCqVec : (int)left);
 #pragma unroll
             for (int j = 0; j < kCqVec; ++j)
-                if (j < nvalid) store1<EBF>(sg.e, i0 + j, en[j]);
+                if (j < nvalid) store1<EK>(sg.e, i0 + j, en[j], p.err_scale);
             const int nbytes = (nvalid * BITS + 7) / 8;
             uint8_t* c = sg.codes + (i0 * BITS) / 8;
 #pragma unroll
@@ -194,61 +216,70 @@ __device__ __forceinline__ int find_segment(const CqParams& p, int64_t t) {
     return lo;
 }
 
-template <bool GBF, bool EBF, int BITS, int B, bool FIXED>
+template <int GK, int EK, int BITS, int B, bool FIXED>
 __global__ __launch_bounds__(kCqThreads) void cq_kernel(CqParams p) {
     const int lane = lane_id();
     const int64_t nwaves = (int64_t)gridDim.x * (kCqThreads / kWave);
-    const int64_t wg = xcd_remap<kXcds, kCqXcdRun>(blockIdx.x, gridDim.x);
+    constexpr int TILE = cq_tile_elems(EK);
+    const int64_t wg = xcd_remap<kXcds, EK == kI8 ? kCqXcdRunI8 : kCqXcdRun>(blockIdx.x, gridDim.x);
     for (int64_t t = wg * (kCqThreads / kWave) + uniform(threadIdx.x / kWave); t < p.ntiles;
          t += nwaves) {
         const CqSegDev sg = p.seg[find_segment(p, t)];
-        const int64_t base = (t - sg.tile0) * kCqTile;
-        if (base + kCqTile <= sg.n)
-            cq_tile<GBF, EBF, BITS, B, FIXED, true>(sg, base, lane, p);
+        const int64_t base = (t - sg.tile0) * TILE;
+        if (base + TILE <= sg.n)
+            cq_tile<GK, EK, BITS, B, FIXED, true>(sg, base, lane, p);
         else
-            cq_tile<GBF, EBF, BITS, B, FIXED, false>(sg, base, lane, p);
+            cq_tile<GK, EK, BITS, B, FIXED, false>(sg, base, lane, p);
     }
 }
 
-template <bool GBF, bool EBF, int BITS, bool FIXED>
+template <int GK, int EK, int BITS, bool FIXED>
 const void* pick_block(int block) {
     if constexpr (FIXED) {
-        return (const void*)&cq_kernel<GBF, EBF, BITS, 64, true>;
+        return (const void*)&cq_kernel<GK, EK, BITS, 64, true>;
     } else {
         switch (block) {
-            case 64: return (const void*)&cq_kernel<GBF, EBF, BITS, 64, false>;
-            case 128: return (const void*)&cq_kernel<GBF, EBF, BITS, 128, false>;
-            case 256: return (const void*)&cq_kernel<GBF, EBF, BITS, 256, false>;
-            case 512: return (const void*)&cq_kernel<GBF, EBF, BITS, 512, false>;
+            case 64: return (const void*)&cq_kernel<GK, EK, BITS, 64, false>;
+            case 128: return (const void*)&cq_kernel<GK, EK, BITS, 128, false>;
+            case 256: return (const void*)&cq_kernel<GK, EK, BITS, 256, false>;
+            case 512: return (const void*)&cq_kernel<GK, EK, BITS, 512, false>;
         }
         return nullptr;
     }
 }
 
-template <bool GBF, bool EBF, bool FIXED>
+template <int GK, int EK, bool FIXED>
 const void* pick_bits(int bits, int block) {
     switch (bits) {
-        case 2: return pick_block<GBF, EBF, 2, FIXED>(block);
-        case 4: return pick_block<GBF, EBF, 4, FIXED>(block);
-        case 8: return pick_block<GBF, EBF, 8, FIXED>(block);
+        case 2: return pick_block<GK, EK, 2, FIXED>(block);
+        case 4: return pick_block<GK, EK, 4, FIXED>(block);
+        case 8: return pick_block<GK, EK, 8, FIXED>(block);
     }
     return nullptr;
 }
 
-template <bool GBF, bool EBF>
+template <int GK, int EK>
 const void* pick_fixed(bool fixed, int bits, int block) {
-    return fixed ? pick_bits<GBF, EBF, true>(bits, block) : pick_bits<GBF, EBF, false>(bits, block);
+    return fixed ? pick_bits<GK, EK, true>(bits, block) : pick_bits<GK, EK, false>(bits, block);
+}
+
+template <int GK>
+const void* pick_err(int err_kind, bool fixed, int bits, int block) {
+    switch (err_kind) {
+        case kF32: return pick_fixed<GK, kF32>(fixed, bits, block);
+        case kBF16: return pick_fixed<GK, kBF16>(fixed, bits, block);
+        case kI8: return pick_fixed<GK, kI8>(fixed, bits, block);
+    }
+    return nullptr;
 }
 
 }  // namespace
 
-hipError_t launch_cq(const CqParams& p, bool grad_bf16, bool err_bf16, int bits, int block,
-                     bool fixed, hipStream_t stream) {
+hipError_t launch_cq(const CqParams& p, int grad_kind, int err_kind, int bits, int block, bool fixed,
+                     hipStream_t stream) {
     const void* k = nullptr;
-    if (grad_bf16)
-        k = err_bf16 ? pick_fixed<true, true>(fixed, bits, block) : pick_fixed<true, false>(fixed, bits, block);
-    else
-        k = err_bf16 ? pick_fixed<false, true>(fixed, bits, block) : pick_fixed<false, false>(fixed, bits, block);
+    if (grad_kind == kBF16) k = pick_err<kBF16>(err_kind, fixed, bits, block);
+    else if (grad_kind == kF32) k = pick_err<kF32>(err_kind, fixed, bits, block);
     if (!k) return hipErrorInvalidValue;
     const int64_t waves_per_block = kCqThreads / kWave;
     int64_t blocks = (p.ntiles + waves_per_block - 1) / waves_per_block;

@@ -34,18 +34,6 @@ __device__ __forceinline__ int code_of(u32x2 w, int j) {
     else return __builtin_amdgcn_sbfe(w.x, j * BITS, BITS);
 }
 
-// v_cvt_f32_ubyteN: byte N of x as a float, in one instruction (the compiler otherwise
-// extracts the byte with a separate bit-field op first).
-template <int N>
-__device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
-    float r;
-    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
-    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
-    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
-    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
-    return r;
-}
-
 template <int N>
 __device__ __forceinline__ void acc_byte(float& a, uint32_t x, float step, float off) {
     a = a + __builtin_fmaf(ubyte_to_f32<N>(x), step, off);

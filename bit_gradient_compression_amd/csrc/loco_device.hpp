@@ -31,6 +31,18 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
     return __builtin_bit_cast(uint16_t, a);
 }
 
+// v_cvt_f32_ubyteN: byte N of x as a float, in one instruction (the compiler otherwise
+// extracts the byte with a separate bit-field op first).
+template <int N>
+__device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
+    float r;
+    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 // ---- wavefront primitives -------------------------------------------------------
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

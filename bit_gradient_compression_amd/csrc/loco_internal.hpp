@@ -14,6 +14,12 @@ namespace loco {
 #ifndef LOCO_CQ_UNROLL
 #define LOCO_CQ_UNROLL 1
 #endif
+#ifndef LOCO_CQ_UNROLL_I8
+#define LOCO_CQ_UNROLL_I8 4
+#endif
+#ifndef LOCO_CQ_XCD_RUN_I8
+#define LOCO_CQ_XCD_RUN_I8 32
+#endif
 #ifndef LOCO_CQ_THREADS
 #define LOCO_CQ_THREADS 256
 #endif
@@ -41,6 +47,7 @@ constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 // than the identity.
 constexpr int kXcds = 8;
 constexpr int kCqXcdRun = LOCO_CQ_XCD_RUN;
+constexpr int kCqXcdRunI8 = LOCO_CQ_XCD_RUN_I8;
 constexpr int kDrXcdRun = LOCO_DR_XCD_RUN;
 
 // Segments per launch; a call with more segments is split into several launches.
@@ -48,7 +55,11 @@ constexpr int kCqMaxSeg = 32;
 // Elements per lane per sub-tile, and sub-tiles per wave tile.
 constexpr int kCqVec = 8;
 constexpr int kCqUnroll = LOCO_CQ_UNROLL;
-constexpr int kCqTile = 64 * kCqVec * kCqUnroll;  // elements per wave tile
+// An int8 error moves 4.5 B per element instead of 10.5, so its waves take more sub-tiles
+// to keep as many bytes in flight.
+constexpr int kCqUnrollI8 = LOCO_CQ_UNROLL_I8;
+constexpr int cq_unroll(int err_kind) { return err_kind == 2 ? kCqUnrollI8 : kCqUnroll; }
+constexpr int cq_tile_elems(int err_kind) { return 64 * kCqVec * cq_unroll(err_kind); }  // per wave tile
 constexpr int kCqThreads = LOCO_CQ_THREADS;
 
 struct CqSegDev {
@@ -66,9 +77,12 @@ struct CqParams {
     int64_t ntiles;
     float beta, omega;            // e' = beta*e + omega*r, omega = fl(1 - beta)
     float fixed_inv, fixed_step;  // fixed-scale mode: inv = s, step = fl(1/s)
+    float err_scale, err_step;    // 8-bit error: e8 = clamp(rint(e*s_e)), e = e8*fl(1/s_e)
+    int reset;                    // nonzero: store e' = 0 this step
 };
 
-hipError_t launch_cq(const CqParams& p, bool grad_bf16, bool err_bf16, int bits, int block,
+// Element kinds: grad_kind 0 fp32 / 1 bf16; err_kind 0 fp32 / 1 bf16 / 2 int8 codes.
+hipError_t launch_cq(const CqParams& p, int grad_kind, int err_kind, int bits, int block,
                      bool fixed, hipStream_t stream);
 
 // ---- dequant-reduce ---------------------------------------------------------------

@@ -17,6 +17,7 @@ from . import build as _build
 
 LOCO_F32 = 0
 LOCO_BF16 = 1
+LOCO_I8 = 2
 LOCO_OK = 0
 LOCO_ERR_INVALID = -1
 LOCO_ERR_ALIGN = -2
@@ -24,8 +25,8 @@ LOCO_ERR_UNSUPPORTED = -3
 LOCO_ERR_HIP = -4
 LOCO_MAX_PEERS = 128
 
-SYMBOLS = ["loco_compensate_quantize", "loco_dequant_reduce", "loco_topk_quantize",
-           "loco_status_string", "loco_version"]
+SYMBOLS = ["loco_compensate_quantize", "loco_compensate_quantize_ex", "loco_dequant_reduce",
+           "loco_topk_quantize", "loco_status_string", "loco_version"]
 
 
 class LocoError(RuntimeError):
@@ -37,6 +38,12 @@ class LocoError(RuntimeError):
 class CqSegment(ctypes.Structure):
     _fields_ = [("grad", ctypes.c_void_p), ("err", ctypes.c_void_p), ("codes", ctypes.c_void_p),
                 ("absmax", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+class CqOptions(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int), ("block", ctypes.c_int), ("beta", ctypes.c_float),
+                ("fixed_scale", ctypes.c_float), ("err_scale", ctypes.c_float),
+                ("reset_error", ctypes.c_int)]
 
 
 class Payload(ctypes.Structure):
@@ -63,6 +70,9 @@ def load(path: str | None = None):
                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                              ctypes.c_float, ctypes.c_void_p]
     lib.loco_compensate_quantize.restype = ctypes.c_int
+    lib.loco_compensate_quantize_ex.argtypes = [ctypes.POINTER(CqSegment), ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.POINTER(CqOptions), ctypes.c_void_p]
+    lib.loco_compensate_quantize_ex.restype = ctypes.c_int
     lib.loco_dequant_reduce.argtypes = [ctypes.POINTER(Payload), ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
                                         ctypes.c_int, ctypes.c_void_p]
@@ -96,6 +106,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return LOCO_F32
     if t.dtype == torch.bfloat16:
         return LOCO_BF16
+    if t.dtype == torch.int8:
+        return LOCO_I8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -125,10 +137,7 @@ def num_blocks(n: int, block: int) -> int:
     return -(-n // block)
 
 
-def loco_compensate_quantize(segments, *, bits: int, block: int, beta: float, fixed_scale: float = 0.0,
-                             stream=None, grad_dtype=None, err_dtype=None) -> None:
-    """segments: iterable of (grad, err, codes, absmax) tensors; absmax may be None in
-    fixed-scale mode.  n of a segment is grad.numel()."""
+def _segments(segments):
     segs = list(segments)
     arr = (CqSegment * max(1, len(segs)))()
     gd = ed = None
@@ -138,12 +147,35 @@ def loco_compensate_quantize(segments, *, bits: int, block: int, beta: float, fi
         if _dtype_code(g) != gd or _dtype_code(e) != ed:
             raise TypeError("all segments must share grad and err dtypes")
         arr[i] = CqSegment(_ptr(g), _ptr(e), _ptr(c), _ptr(a), g.numel())
+    return arr, len(segs), gd, ed
+
+
+def loco_compensate_quantize(segments, *, bits: int, block: int, beta: float, fixed_scale: float = 0.0,
+                             stream=None, grad_dtype=None, err_dtype=None) -> None:
+    """segments: iterable of (grad, err, codes, absmax) tensors; absmax may be None in
+    fixed-scale mode.  n of a segment is grad.numel()."""
+    arr, nseg, gd, ed = _segments(segments)
     gd = gd if grad_dtype is None else grad_dtype
     ed = ed if err_dtype is None else err_dtype
-    st = load().loco_compensate_quantize(arr, len(segs), LOCO_F32 if gd is None else gd,
+    st = load().loco_compensate_quantize(arr, nseg, LOCO_F32 if gd is None else gd,
                                          LOCO_F32 if ed is None else ed, bits, block, beta,
                                          fixed_scale, _stream(stream))
     _check("loco_compensate_quantize", st)
+
+
+def loco_compensate_quantize_ex(segments, *, bits: int, block: int, beta: float, fixed_scale: float = 0.0,
+                                err_scale: float = 0.0, reset_error: bool = False, stream=None,
+                                grad_dtype=None, err_dtype=None) -> None:
+    """As loco_compensate_quantize; an int8 err tensor holds the 8-bit error of scale
+    err_scale, and reset_error stores a zero error this step."""
+    arr, nseg, gd, ed = _segments(segments)
+    gd = gd if grad_dtype is None else grad_dtype
+    ed = ed if err_dtype is None else err_dtype
+    opt = CqOptions(bits, block, beta, fixed_scale, err_scale, 1 if reset_error else 0)
+    st = load().loco_compensate_quantize_ex(arr, nseg, LOCO_F32 if gd is None else gd,
+                                            LOCO_F32 if ed is None else ed, ctypes.byref(opt),
+                                            _stream(stream))
+    _check("loco_compensate_quantize_ex", st)
 
 
 def loco_dequant_reduce(peers, n: int, *, bits: int, block: int, out, out_scale: float,
@@ -169,5 +201,6 @@ def loco_topk_quantize(grad, err, *, chunk: int, k: int, idx, codes, absmax, bit
 
 # short names
 compensate_quantize = loco_compensate_quantize
+compensate_quantize_ex = loco_compensate_quantize_ex
 dequant_reduce = loco_dequant_reduce
 topk_quantize = loco_topk_quantize

@@ -38,17 +38,19 @@
 extern "C" {
 #endif
 
-/* Element types of gradients, errors and outputs. */
-typedef enum { LOCO_F32 = 0, LOCO_BF16 = 1 } loco_dtype_t;
+/* Element types of gradients, errors and outputs.  LOCO_I8 is only an error type of
+ * loco_compensate_quantize_ex: the paper's 8-bit error codes of a fixed scale s_e. */
+typedef enum { LOCO_F32 = 0, LOCO_BF16 = 1, LOCO_I8 = 2 } loco_dtype_t;
 
 /* Status codes: 0 ok, < 0 error (nothing launched). */
 #define LOCO_OK 0
 #define LOCO_ERR_INVALID (-1)     /* bad size, bits, block, k, chunk, beta, scale, dtype,
-                                     null pointer, or overlapping buffers */
+                                     peer count < 1, null pointer, or overlapping buffers */
 #define LOCO_ERR_ALIGN (-2)       /* a device pointer is not 16-byte aligned */
 #define LOCO_ERR_UNSUPPORTED (-3) /* valid but not built: bits not in {2,4,8}, block not
                                      in {64,128,256,512}, chunk not in
-                                     {256,512,1024,2048,4096}, too many segments/peers */
+                                     {256,512,1024,2048,4096}, more than LOCO_MAX_PEERS
+                                     peers */
 #define LOCO_ERR_HIP (-4)         /* the HIP launch failed */
 
 /* Largest number of peers one dequant-reduce call accepts. */
@@ -60,7 +62,8 @@ typedef enum { LOCO_F32 = 0, LOCO_BF16 = 1 } loco_dtype_t;
  * segment, so each segment's payload is self-contained (one all2all partition,
  * LoCo Sec. 3.3).
  *   grad    device, n elements of grad_dtype (read)
- *   err     device, n elements of err_dtype, read and updated in place
+ *   err     device, n elements of err_dtype (4, 2 or 1 bytes each), read and
+ *           updated in place
  *   codes   device, ceil(n*bits/8) bytes (written); codes are two's complement,
  *           packed little end first (4 bits: element 2j in the low nibble of byte j;
  *           2 bits: element 4j+t at bits 2t of byte j); unused high bits of the last
@@ -98,12 +101,43 @@ typedef struct {
  *   block       64, 128, 256 or 512 (ignored when fixed_scale > 0)
  *   beta        in [0, 1]
  *   fixed_scale 0 for per-block absmax scales, or a finite s > 0
+ * Any number of segments is accepted (they are launched 32 at a time, in order).
+ * err_dtype LOCO_I8 is refused here (LOCO_ERR_INVALID): it needs the error scale of
+ * loco_compensate_quantize_ex.
  * Returns LOCO_OK or an error status.
  */
 int loco_compensate_quantize(const loco_cq_segment_t* segs, int nseg,
                              loco_dtype_t grad_dtype, loco_dtype_t err_dtype,
                              int bits, int block, float beta, float fixed_scale,
                              void* stream);
+
+/* Options of loco_compensate_quantize_ex (a host struct, read during the call). */
+typedef struct {
+    int bits;          /* 2, 4 or 8 */
+    int block;         /* 64, 128, 256 or 512 (ignored when fixed_scale > 0) */
+    float beta;        /* in [0, 1] */
+    float fixed_scale; /* 0, or a finite s > 0 */
+    float err_scale;   /* s_e of an 8-bit error (err_dtype LOCO_I8); ignored otherwise */
+    int reset_error;   /* nonzero: this step stores e = 0 */
+} loco_cq_options_t;
+
+/*
+ * loco_compensate_quantize_ex - loco_compensate_quantize plus LoCo Sec. 3.2, Eqn. (7):
+ * the compensation error kept in 8 bits, and its periodic reset.
+ *
+ * Same segments, arithmetic and outputs as loco_compensate_quantize, with:
+ *   err_dtype LOCO_I8: err holds n int8 codes e8 of the scale s_e = err_scale, which
+ *     must be finite, > 0, with 256 / s_e finite.  On load e = e8 * fl(1 / s_e) (the
+ *     decompressor of Eqn. (1) with the error's own scale); on store
+ *     e8 <- clamp(rint(e * s_e), -128, 127), ties to even (Eqn. (7)).
+ *   reset_error != 0: the codes and absmax are those of h = g + e as usual, but the
+ *     stored error is 0 (Eqn. (7) resets the error every T_c steps; the caller
+ *     passes reset_error on those steps).  Any err_dtype.
+ * Returns LOCO_OK or an error status (LOCO_ERR_INVALID for a NULL opt).
+ */
+int loco_compensate_quantize_ex(const loco_cq_segment_t* segs, int nseg,
+                                loco_dtype_t grad_dtype, loco_dtype_t err_dtype,
+                                const loco_cq_options_t* opt, void* stream);
 
 /* One peer's payload for a partition: what loco_compensate_quantize wrote. */
 typedef struct {

@@ -170,3 +170,48 @@ def test_tk_checks(lib, kwargs, want):
 def test_tk_noop(lib):
     assert tk(lib, n=0) == OK
     assert tk(lib, n=0, g=0) == OK
+
+
+I8 = loco.LOCO_I8
+
+
+def cqx(lib, segs, gd=F32, ed=I8, bits=4, block=128, beta=0.9, fixed=0.0, err_scale=256.0, reset=0,
+        opt=True):
+    arr = (loco.CqSegment * max(1, len(segs)))(*segs) if segs else None
+    o = loco.CqOptions(bits, block, beta, fixed, err_scale, reset)
+    return lib.loco_compensate_quantize_ex(arr, len(segs), gd, ed, ctypes.byref(o) if opt else None, None)
+
+
+@pytest.mark.parametrize("kwargs,want", [
+    (dict(opt=False), INV),
+    (dict(gd=I8), INV), (dict(ed=3), INV),
+    (dict(err_scale=0.0), INV), (dict(err_scale=-4.0), INV), (dict(err_scale=NAN), INV),
+    (dict(err_scale=math.inf), INV),
+    (dict(err_scale=1e-37), INV),          # 256 / s_e overflows binary32
+    (dict(bits=3), UNSUP), (dict(block=100), UNSUP), (dict(beta=2.0), INV), (dict(fixed=-1.0), INV),
+    (dict(reset=1, bits=5), UNSUP),
+])
+def test_cq_ex_parameter_checks(lib, kwargs, want):
+    assert cqx(lib, [seg()], **kwargs) == want
+
+
+def test_cq_ex_err_scale_ignored_for_float_errors(lib):
+    # a float error never reads s_e: only the segment's misalignment is reported
+    assert cqx(lib, [seg(g=A + 2)], ed=F32, err_scale=0.0) == ALIGN
+    assert cqx(lib, [seg(g=A + 2)], ed=BF16, err_scale=NAN) == ALIGN
+
+
+def test_cq_old_entry_refuses_int8_error(lib):
+    assert cq(lib, [seg()], ed=I8) == INV
+
+
+def test_cq_ex_int8_error_is_one_byte_per_element(lib):
+    # codes start 1008 bytes after an int8 error of 1000 elements: no overlap at one byte
+    # per element (an f32 error would cover 4000 bytes and overlap them).  The second
+    # segment is misaligned, so the call stops at ALIGN and launches nothing.
+    first = seg(e=Bp, c=Bp + 1008, a=Dp)
+    bad = seg(g=A + 8192 + 2, e=Bp + 65536, c=Cp, a=Dp + 65536)
+    assert cqx(lib, [first, bad]) == ALIGN
+    assert cqx(lib, [first, bad], ed=F32) == INV
+    # and an overlap inside the int8 error's 1000 bytes is still refused
+    assert cqx(lib, [seg(e=Bp, c=Bp + 992)]) == INV

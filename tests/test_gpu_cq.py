@@ -17,7 +17,7 @@ from parity_util import (Guarded, assert_bf16_close, assert_bytes_equal, assert_
 
 pytestmark = pytest.mark.gpu
 
-TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+TD = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
 EDGE_SIZES = [1, 0, 7, 8, 9, 511, 512, 513, 1023, 1024, 1025, 4099, 65536 + 17]
 
 
@@ -32,13 +32,19 @@ def grads(step, n, gd, key, scale=None):
 
 
 def storage(t, dt):
-    """CPU tensor -> the oracle's storage form (float32, or uint16 bf16 patterns)."""
+    """CPU tensor -> the oracle's storage form (float32, int8, or uint16 bf16 patterns)."""
     if dt == "bf16":
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
     return t.contiguous().numpy()
 
 
-def run_chain(loco, sizes, gd, ed, bits, block, beta, steps, fixed=0.0, gen=None, key="cq"):
+ORA_E = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}
+
+
+def run_chain(loco, sizes, gd, ed, bits, block, beta, steps, fixed=0.0, gen=None, key="cq", err_scale=0.0,
+              reset_every=0):
+    """reset_every = T_c > 0 resets the error on steps T_c - 1, 2 T_c - 1, ... (Eqn. (7));
+    an int8 error ('i8') has the scale err_scale.  Both go through the _ex entry point."""
     segs = []
     for n in sizes:
         g = Guarded(n, TD[gd])
@@ -46,7 +52,8 @@ def run_chain(loco, sizes, gd, ed, bits, block, beta, steps, fixed=0.0, gen=None
         c = Guarded(loco.code_bytes(n, bits), torch.uint8)
         a = None if fixed else Guarded(loco.num_blocks(n, block), torch.float32)
         segs.append((g, e, c, a))
-    e_ora = [np.zeros(n, np.float32 if ed == "f32" else np.uint16) for n in sizes]
+    e_ora = [np.zeros(n, ORA_E[ed]) for n in sizes]
+    use_ex = ed == "i8" or reset_every > 0
     bitwise = True
     total = sum(sizes)
     for step in range(steps):
@@ -55,20 +62,29 @@ def run_chain(loco, sizes, gd, ed, bits, block, beta, steps, fixed=0.0, gen=None
         for (g, _, _, _), n in zip(segs, sizes):
             g.t.copy_(gall[off:off + n])
             off += n
-        loco.loco_compensate_quantize([(g.t, e.t, c.t, None if a is None else a.t) for g, e, c, a in segs],
-                                      bits=bits, block=block, beta=beta, fixed_scale=fixed)
+        reset = reset_every > 0 and (step + 1) % reset_every == 0
+        args = [(g.t, e.t, c.t, None if a is None else a.t) for g, e, c, a in segs]
+        if use_ex:
+            loco.loco_compensate_quantize_ex(args, bits=bits, block=block, beta=beta, fixed_scale=fixed,
+                                             err_scale=err_scale, reset_error=reset)
+        else:
+            loco.loco_compensate_quantize(args, bits=bits, block=block, beta=beta, fixed_scale=fixed)
         torch.cuda.synchronize()
         off = 0
         for i, ((g, e, c, a), n) in enumerate(zip(segs, sizes)):
             gn = storage(gall[off:off + n], gd)
             off += n
             ref = oracle.compensate_quantize(gn, e_ora[i], bits=bits, block=block, beta=beta,
-                                             fixed_scale=fixed, grad_dtype=gd, err_dtype=ed)
+                                             fixed_scale=fixed, grad_dtype=gd, err_dtype=ed,
+                                             err_scale=err_scale, reset=reset)
             tag = f"step {step} segment {i} (n={n})"
             assert_bytes_equal(host(c.t), ref["codes"], f"{tag} codes")
             if a is not None:
                 assert_bytes_equal(host(a.t).view(np.uint32), ref["absmax"].view(np.uint32), f"{tag} absmax")
-            if ed == "f32":
+            if ed == "i8":
+                # the 8-bit codes are integer decisions taken in fp32 on both sides: bit-exact
+                assert_bytes_equal(host(e.t), ref["e_new"], f"{tag} 8-bit error")
+            elif ed == "f32":
                 floor = (step_per_elem(ref["absmax"], bits, block, n) if a is not None
                          else np.full(n, 1.0 / fixed))
                 bitwise &= assert_f32_close(host(e.t), ref["e_new"], floor, f"{tag} error")
@@ -186,3 +202,53 @@ def test_cq_deterministic_and_stream(gpu_lib):
         outs.append((host(c), host(a), host(e)))
     for x, y in zip(outs[0], outs[1]):
         assert np.array_equal(x, y)
+
+
+# -- the paper's 8-bit error and its periodic reset (LoCo Sec. 3.2, Eqn. (7)) ---------------
+
+@pytest.mark.parametrize("s_e", [2.0 ** 18, 300_000.0])
+def test_cq_i8_error_tiny(gpu_lib, s_e):
+    """The tiny workload with the error in 8 bits (s_e a power of two, and not), reset
+    every T_c = 5 steps, 12 steps."""
+    say(f"cq i8 error tiny: s_e={s_e} T_c=5 x12")
+    run_chain(gpu_lib, [W.TINY_N], "f32", "i8", 4, 128, 0.9, 12, gen=lambda s, n: W.tiny_grad(s, n=n),
+              err_scale=s_e, reset_every=5)
+
+
+@pytest.mark.parametrize("gd", ["f32", "bf16"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("block", [64, 512])
+def test_cq_i8_matrix(gpu_lib, gd, bits, block):
+    """8-bit error with every code width on the ragged multi-segment sizes."""
+    say(f"cq i8 matrix {gd} bits={bits} B={block}")
+    run_chain(gpu_lib, EDGE_SIZES, gd, "i8", bits, block, 0.9, 3, key="i8matrix", err_scale=2.0 ** 18)
+
+
+@pytest.mark.parametrize("s_e", [2.0 ** 22, 5.0e6])
+def test_cq_i8_error_clamps(gpu_lib, s_e):
+    """A scale too large for the error's range: many codes clamp at -128 and 127."""
+    say(f"cq i8 clamping s_e={s_e}")
+    run_chain(gpu_lib, [70_001, 513], "bf16", "i8", 4, 256, 0.9, 4, key="i8clamp", err_scale=s_e)
+
+
+def test_cq_i8_fixed_scale(gpu_lib):
+    """Eqn. (1) with a global scale and the error in 8 bits: the paper's own configuration."""
+    say("cq i8 + fixed scale")
+    run_chain(gpu_lib, [1000, 70_001], "bf16", "i8", 4, 128, 0.9, 4, fixed=2.0 ** 19,
+              gen=lambda st, n: grads(st, n, "bf16", "i8fixed", scale=1e-2), err_scale=2.0 ** 21)
+
+
+@pytest.mark.parametrize("ed", ["f32", "bf16"])
+def test_cq_reset_float_error(gpu_lib, ed):
+    """The reset of Eqn. (7) on a float error: reset on every other step."""
+    say(f"cq reset every 2 steps, {ed} error")
+    run_chain(gpu_lib, EDGE_SIZES, "bf16", ed, 4, 128, 0.9, 5, key="reset", reset_every=2)
+
+
+def test_cq_i8_llama_layer_scaled(gpu_lib):
+    """The LLaMA-7B layer recipe with rows / 64, 8-bit error, T_c = 4."""
+    shapes = W.llama_layer_shapes(64)
+    sizes = [r * c for _, r, c in shapes]
+    say(f"cq i8 llama layer /64: {sizes}")
+    run_chain(gpu_lib, sizes, "bf16", "i8", 4, 128, 0.9, 6,
+              gen=lambda s, n: torch.cat(W.llama_layer_grads(s, div=64)), err_scale=2.0 ** 18, reset_every=4)

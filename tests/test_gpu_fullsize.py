@@ -15,7 +15,8 @@ from parity_util import assert_bf16_close, assert_bytes_equal, assert_f32_close,
 
 pytestmark = pytest.mark.gpu
 
-TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+TD = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+ORA_E = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}
 
 
 def block_ranges(nblocks, rng, count=24, run=3):
@@ -36,7 +37,7 @@ def storage(t, dt):
     return t.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
 
 
-def fullsize_cq(loco, sizes, gd, ed, bits, block, beta, steps, gen, tag, seed=0):
+def fullsize_cq(loco, sizes, gd, ed, bits, block, beta, steps, gen, tag, seed=0, err_scale=0.0, reset_every=0):
     dev = "cuda"
     rng = np.random.default_rng(seed)
     e = [torch.zeros(n, dtype=TD[ed], device=dev) for n in sizes]
@@ -47,25 +48,33 @@ def fullsize_cq(loco, sizes, gd, ed, bits, block, beta, steps, gen, tag, seed=0)
     for s, n in enumerate(sizes):
         for b0, b1 in ranges[s]:
             m = min(b1 * block, n) - b0 * block
-            ora_e[(s, b0)] = np.zeros(m, np.float32 if ed == "f32" else np.uint16)
+            ora_e[(s, b0)] = np.zeros(m, ORA_E[ed])
     checked = 0
     bitwise = True
     for step in range(steps):
         say(f"{tag}: step {step}: generating and launching ({sum(sizes):,} elements, {len(sizes)} segments)")
         gs = gen(step)
         assert [g.numel() for g in gs] == list(sizes)
-        loco.loco_compensate_quantize(list(zip(gs, e, codes, absmax)), bits=bits, block=block, beta=beta)
+        reset = reset_every > 0 and (step + 1) % reset_every == 0
+        if ed == "i8" or reset_every:
+            loco.loco_compensate_quantize_ex(list(zip(gs, e, codes, absmax)), bits=bits, block=block, beta=beta,
+                                             err_scale=err_scale, reset_error=reset)
+        else:
+            loco.loco_compensate_quantize(list(zip(gs, e, codes, absmax)), bits=bits, block=block, beta=beta)
         torch.cuda.synchronize()
         for s, n in enumerate(sizes):
             for b0, b1 in ranges[s]:
                 lo, hi = b0 * block, min(b1 * block, n)
                 ref = oracle.compensate_quantize(storage(gs[s][lo:hi], gd), ora_e[(s, b0)], bits=bits, block=block,
-                                                 beta=beta, grad_dtype=gd, err_dtype=ed)
+                                                 beta=beta, grad_dtype=gd, err_dtype=ed, err_scale=err_scale,
+                                                 reset=reset)
                 t = f"{tag} step {step} seg {s} blocks {b0}:{b1}"
                 assert_bytes_equal(host(codes[s][lo * bits // 8:(hi * bits + 7) // 8]), ref["codes"], f"{t} codes")
                 assert_bytes_equal(host(absmax[s][b0:b1]).view(np.uint32), ref["absmax"].view(np.uint32),
                                    f"{t} absmax")
-                if ed == "f32":
+                if ed == "i8":
+                    assert_bytes_equal(host(e[s][lo:hi]), ref["e_new"], f"{t} 8-bit error")
+                elif ed == "f32":
                     bitwise &= assert_f32_close(host(e[s][lo:hi]), ref["e_new"],
                                                 step_per_elem(ref["absmax"], bits, block, hi - lo), f"{t} error")
                 else:
@@ -85,6 +94,17 @@ def test_fullsize_7b_shard(gpu_lib, bits, steps):
         g = W.shard7b_grad(step, n=W.SHARD7B_N, device="cuda", chain=f"full{bits}")
         return [g[i * part:(i + 1) * part] for i in range(P)]
     fullsize_cq(gpu_lib, [part] * P, "bf16", "f32", bits, 256, 0.9, steps, gen, f"7b-shard {bits}-bit")
+
+
+def test_fullsize_7b_shard_i8_error(gpu_lib):
+    """The 7B shard with the paper's 8-bit error (s_e = 2^17) reset every T_c = 3 steps, 4 steps."""
+    part, P = W.SHARD7B_PART, W.SHARD7B_PEERS
+
+    def gen(step):
+        g = W.shard7b_grad(step, n=W.SHARD7B_N, device="cuda", chain="full-i8")
+        return [g[i * part:(i + 1) * part] for i in range(P)]
+    fullsize_cq(gpu_lib, [part] * P, "bf16", "i8", 4, 256, 0.9, 4, gen, "7b-shard 4-bit, 8-bit error",
+                seed=8, err_scale=2.0 ** 17, reset_every=3)
 
 
 def test_fullsize_llama_layer(gpu_lib):
