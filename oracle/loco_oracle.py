@@ -23,7 +23,8 @@ extracted text, so each step below is rebuilt from the prose around the equation
       of the decompressed low-bit gradients, computed in high precision; with FSDP
       each node averages only its own partition (all2all, then a local average).
 * "Communication Efficient LLM Pre-training with SparseLoCo" (summary and
-  abstract): Top-k sparsification, 2-bit quantisation and error feedback.
+  abstract): Top-k sparsification, 2-bit quantisation and error feedback, and a
+  sparse aggregation of the nodes' sparse updates.
 
 Readings where the pages are silent (each is also listed in the design notes):
 * per-block absmax scale: the stored scale is the block's max |h| (exact); the
@@ -36,6 +37,9 @@ Readings where the pages are silent (each is also listed in the design notes):
 * SparseLoCo: per-chunk Top-k by |h| (compared as the bit pattern of |h|), ties to
   the lower index; the kept values get codes of the same quantiser with b = 2 and
   the chunk's absmax; error feedback h = g + decay * e, e' = h - transmitted.
+* SparseLoCo's sparse aggregation: the high-precision average of LoCo Eqn. (8)
+  applied to the peers' sparse payloads (each scattered into a dense zero vector),
+  accumulated in peer order.
 
 The functions are generic over the float type of their inputs: called with
 float32 arrays they are the parity oracle; called with float64 arrays they are
@@ -365,6 +369,49 @@ def topk_quantize(g, e, *, chunk, k, bits=2, decay=1.0, ftype=np.float32):
         absmax_out[c] = absmax
     return {"idx": idx_out.reshape(-1), "codes": codes_out.reshape(-1),
             "absmax": absmax_out, "e_new": e_new, "h": h}
+
+
+def sparse_aggregate(payloads, n, *, chunk, k, bits, out_scale, out_dtype="f32", ftype=np.float32):
+    """SparseLoCo's sparse aggregation of the peers' Top-k payloads (summary and
+    abstract), read as the high-precision average of LoCo Sec. 3.3, Eqn. (8) over
+    sparse vectors:
+      acc = 0
+      for p = 0 .. N-1 (in that order), for every chunk c and used slot j of peer p:
+          acc[c*chunk + idx_p[c, j]] = acc[...] + q_p[c, j] * step_p[c]
+      out = acc * out_scale
+    with step_p[c] = absmax_p[c] / qmax (0 when absmax is 0).  A slot is used when
+    its index lies inside its chunk (the last chunk may be short); unused slots hold
+    0xFFFF.  The slots of one peer's chunk name distinct elements.
+
+    payloads: list of (idx uint16[chunks*k], codes uint8[chunks*ceil(k*bits/8)],
+    absmax float32[chunks]), as topk_quantize writes them.  Returns float32 or bf16
+    patterns (uint16).
+    """
+    nchunks = -(-n // chunk)
+    cbytes = -(-k * bits // 8)
+    per = 8 // bits
+    base = np.arange(nchunks, dtype=np.int64)[:, None] * chunk
+    length = np.minimum(chunk, n - base)
+    acc = np.zeros(n, dtype=ftype)
+    for idx, codes, absmax in payloads:
+        ix = np.asarray(idx, dtype=np.uint16).reshape(nchunks, k).astype(np.int64)
+        rows = np.asarray(codes, dtype=np.uint8).reshape(nchunks, cbytes)
+        # each chunk's codes start on a byte of their own: unpack row by row
+        q = unpack_codes(rows.reshape(-1), bits, nchunks * cbytes * per).reshape(nchunks, -1)[:, :k]
+        step = block_steps(np.asarray(absmax, dtype=ftype), bits)
+        d = dequantize(q, np.repeat(step, k).reshape(nchunks, k))
+        used = ix < length
+        pos = (base + ix)[used]
+        acc[pos] = acc[pos] + d[used]
+    out = acc * ftype(out_scale)
+    if out_dtype == "bf16":
+        return bf16_rne(out.astype(np.float32))
+    return out
+
+
+def sa_algorithmic_bytes(n, npeers, chunk, k, bits, out_bytes):
+    chunks = -(-n // chunk)
+    return npeers * chunks * (2 * k + (-(-k * bits // 8)) + 4) + n * out_bytes
 
 
 def tk_algorithmic_bytes(n, chunk, k, bits=2):

@@ -77,3 +77,21 @@ def topk_cases():
                "codes": bytes.fromhex("".join(c["codes"])),
                "absmax": np.array(c["absmax"], np.float32),
                "e_new": np.array(c["e_new"], np.float32)}
+
+
+def sa_case():
+    d = {"peers": []}
+    for ln in _lines("sa_worked.txt"):
+        k, rest = ln.split(None, 1)
+        if k == "peer":
+            ix, hx, am = rest.split("|")
+            d["peers"].append((np.array(ix.split(), np.int64).astype(np.uint16),
+                               np.frombuffer(bytes.fromhex(hx.replace(" ", "")), np.uint8).copy(),
+                               np.array(am.split(), np.float32)))
+        elif k == "out":
+            d["out"] = np.array(rest.split(), np.float32)
+        elif k == "out_scale":
+            d[k] = float(rest)
+        else:
+            d[k] = int(rest)
+    return d

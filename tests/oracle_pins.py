@@ -420,10 +420,125 @@ def pin_i8_compressor_vs_torch(O):
         assert np.array_equal(O.error_decompress(want, s_e), want.astype(F32) / F32(s_e))
 
 
+# -- SparseLoCo sparse aggregation (SparseLoCo summary; LoCo Sec. 3.3, Eqn. (8)) -----------------
+
+def pin_sa_worked(O):
+    c = golden_io.sa_case()
+    out = O.sparse_aggregate(c["peers"], c["n"], chunk=c["chunk"], k=c["k"], bits=c["bits"],
+                             out_scale=c["out_scale"])
+    assert np.array_equal(out, c["out"]), (out, c["out"])
+
+
+def _sparse_payload(rng, n, chunk, k, bits, ordered=False):
+    """A random valid sparse payload: distinct in-chunk indices (unused slots 0xFFFF),
+    random code bytes, random positive fp32 scales (some chunks zero)."""
+    nch = -(-n // chunk)
+    cb = -(-k * bits // 8)
+    idx = np.full((nch, k), 0xFFFF, np.uint16)
+    for c in range(nch):
+        L = min(chunk, n - c * chunk)
+        m = min(k, L) - int(rng.integers(0, 2))  # sometimes one slot fewer than possible
+        sel = rng.permutation(L)[:max(m, 0)]
+        idx[c, :sel.size] = np.sort(sel) if ordered else sel
+    codes = rng.integers(0, 256, nch * cb).astype(np.uint8)
+    absmax = (rng.random(nch) * 2.0 ** rng.integers(-12, 3, nch)).astype(F32)
+    absmax[rng.random(nch) < 0.1] = 0
+    return idx.reshape(-1), codes, absmax
+
+
+def _sa_brute(peers, n, chunk, k, bits, out_scale):
+    """Element by element from the definition and the packing layout, in fp32 scalars."""
+    qmax = (1 << (bits - 1)) - 1
+    cb = -(-k * bits // 8)
+    acc = [F32(0)] * n
+    for idx, codes, absmax in peers:
+        for c in range(-(-n // chunk)):
+            L = min(chunk, n - c * chunk)
+            a = F32(absmax[c])
+            step = F32(a / F32(qmax)) if a != 0 else F32(0)
+            for j in range(k):
+                i = int(idx[c * k + j])
+                if i >= L:
+                    continue
+                bit = j * bits
+                raw = (int(codes[c * cb + bit // 8]) >> (bit % 8)) & ((1 << bits) - 1)
+                q = raw - (1 << bits) if raw >= (1 << (bits - 1)) else raw
+                acc[c * chunk + i] = F32(acc[c * chunk + i] + F32(F32(q) * step))
+    return np.array([F32(v * F32(out_scale)) for v in acc], F32)
+
+
+def pin_sa_brute_force(O):
+    """Tiny random cases with overlapping indices across peers, ragged last chunks, k*bits
+    not a whole number of bytes, unused slots and zero chunks, against the element-by-
+    element definition; bf16 output against torch's RNE conversion."""
+    rng = _rng(30)
+    for n, chunk, k, bits, npeers in ((29, 8, 3, 2, 3), (50, 16, 9, 4, 4), (37, 8, 6, 8, 5),
+                                      (64, 32, 13, 2, 2), (5, 8, 4, 4, 3)):
+        peers = [_sparse_payload(rng, n, chunk, k, bits) for _ in range(npeers)]
+        scale = 1.0 / 3.0
+        want = _sa_brute(peers, n, chunk, k, bits, scale)
+        got = O.sparse_aggregate(peers, n, chunk=chunk, k=k, bits=bits, out_scale=scale)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (n, chunk, k, bits, got, want)
+        gb = O.sparse_aggregate(peers, n, chunk=chunk, k=k, bits=bits, out_scale=scale, out_dtype="bf16")
+        tb = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(gb, tb)
+
+
+def pin_sa_dense_equivalent(O):
+    """With every slot used (k = chunk) the sparse aggregation is the dense dequant-reduce
+    of the same codes with one scale block per chunk, whatever order the slots take."""
+    rng = _rng(31)
+    for bits in (2, 4, 8):
+        chunk, n, npeers = 16, 16 * 5 + 7, 3
+        qmax = (1 << (bits - 1)) - 1
+        dense, sparse = [], []
+        for _ in range(npeers):
+            q = rng.integers(-qmax - 1, qmax + 1, n)
+            absmax = (rng.random(-(-n // chunk)) * 1e-2).astype(F32)
+            idx = np.full((len(absmax), chunk), 0xFFFF, np.uint16)
+            rows = []
+            for c in range(len(absmax)):
+                L = min(chunk, n - c * chunk)
+                perm = rng.permutation(L)
+                idx[c, :L] = perm
+                qc = np.zeros(chunk, np.int64)
+                qc[:L] = q[c * chunk + perm]
+                rows.append(O.pack_codes(qc, bits))
+            dense.append((O.pack_codes(q, bits), absmax))
+            sparse.append((idx.reshape(-1), np.concatenate(rows), absmax))
+        for od in ("f32", "bf16"):
+            a = O.sparse_aggregate(sparse, n, chunk=chunk, k=chunk, bits=bits, out_scale=1 / 3, out_dtype=od)
+            b = O.dequant_reduce(dense, n, bits=bits, block=chunk, out_scale=1 / 3, out_dtype=od)
+            assert np.array_equal(a, b), (bits, od)
+
+
+def pin_sa_transmits_topk(O):
+    """One peer, scale 1: the aggregation of a Top-k payload is exactly what that step
+    transmitted, h - e' on the kept elements (Sterbenz: h - d is exact there) and 0
+    elsewhere, so transmitted + new error = h."""
+    rng = _rng(32)
+    for bits in (2, 4, 8):
+        n, chunk, k = 64 * 7 + 19, 64, 5
+        g = (rng.standard_normal(n) * 1e-3).astype(F32)
+        e = (rng.standard_normal(n) * 1e-4).astype(F32)
+        r = O.topk_quantize(g, e, chunk=chunk, k=k, bits=bits, decay=0.9)
+        out = O.sparse_aggregate([(r["idx"], r["codes"], r["absmax"])], n, chunk=chunk, k=k, bits=bits,
+                                 out_scale=1.0)
+        kept = np.zeros(n, bool)
+        ix = r["idx"].reshape(-1, k).astype(np.int64)
+        for c in range(ix.shape[0]):
+            kept[c * chunk + ix[c][ix[c] != 0xFFFF]] = True
+        assert kept.sum() == sum(min(k, n - c * chunk) for c in range(ix.shape[0]))
+        sent = r["h"] - r["e_new"]
+        assert np.array_equal(out[kept].view(np.uint32), sent[kept].view(np.uint32))
+        assert not np.any(out[~kept])
+
+
 ALL_PINS = [
     pin_identity_compressor, pin_beta_zero_is_efc, pin_quantisation_bound,
     pin_random_walk_bounded, pin_telescoping, pin_fixed_scale_golden, pin_torch_quantiser,
     pin_topk_brute_force, pin_pack_layout, pin_cq_worked, pin_dr_worked, pin_topk_worked,
     pin_dequant_reduce, pin_zero_blocks, pin_bf16_rne, pin_topk_error_feedback,
     pin_i8_error_accounting, pin_i8_equals_float_when_exact, pin_reset, pin_i8_compressor_vs_torch,
+    pin_sa_worked, pin_sa_brute_force, pin_sa_dense_equivalent, pin_sa_transmits_topk,
 ]

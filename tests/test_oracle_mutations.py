@@ -118,6 +118,32 @@ def _ecomp_no_clamp(e_tilde, s_e):
     return np.rint(e_tilde * ft(s_e)).astype(np.int64).astype(np.int8)
 
 
+def _sa_reversed(payloads, n, **kw):
+    return _orig["sparse_aggregate"](list(payloads)[::-1], n, **kw)
+
+
+def _sa_no_scale(payloads, n, **kw):
+    return _orig["sparse_aggregate"](payloads, n, **dict(kw, out_scale=1.0))
+
+
+def _sa_index_plus_one(payloads, n, **kw):
+    moved = []
+    for idx, codes, absmax in payloads:
+        ix = np.asarray(idx, np.uint16).copy()
+        ix[ix != 0xFFFF] += 1
+        moved.append((ix, codes, absmax))
+    return _orig["sparse_aggregate"](moved, n, **kw)
+
+
+def _sa_slot_scale(payloads, n, **kw):
+    # every chunk decoded with the first chunk's scale
+    out = []
+    for idx, codes, absmax in payloads:
+        a = np.asarray(absmax)
+        out.append((idx, codes, np.resize(a[:1], a.shape) if a.size else a))
+    return _orig["sparse_aggregate"](out, n, **kw)
+
+
 MUTATIONS = {
     "error_update drops beta*e": ("error_update", _drop_beta_term),
     "error_update swaps beta and 1-beta": ("error_update", _swap_weights),
@@ -136,6 +162,10 @@ MUTATIONS = {
     "8-bit error decompressed with s_e, not 1/s_e": ("error_decompress", _edecomp_times_scale),
     "8-bit error compressed with floor": ("error_compress", _ecomp_floor),
     "8-bit error compressed without clamp": ("error_compress", _ecomp_no_clamp),
+    "sparse aggregation in reversed peer order": ("sparse_aggregate", _sa_reversed),
+    "sparse aggregation without out_scale": ("sparse_aggregate", _sa_no_scale),
+    "sparse aggregation index off by one": ("sparse_aggregate", _sa_index_plus_one),
+    "sparse aggregation with the first chunk's scale": ("sparse_aggregate", _sa_slot_scale),
 }
 
 
