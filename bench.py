@@ -7,8 +7,8 @@ A step is one pass of the rank's path on the 7B FSDP-shard workload:
   dequant-reduce of the 8 peer payloads of the rank's own partition into bf16 (x 1/8).
 Inputs are resident in HBM before the timed region; the error buffer carries over from
 step to step.  The SparseLoCo-style Top-k mode (2^28 fp32, chunk 4096, k = 82, 2-bit),
-the 8-bit-code variant and the 8-bit-error variant (LoCo Eqn. (7)) are timed in the same
-run and reported under "modes".
+its sparse aggregation of 8 peers' payloads, the 8-bit-code variant and the 8-bit-error
+variant (LoCo Eqn. (7)) are timed in the same run and reported under "modes".
 
 Prints one JSON line.  value = gradient GB/s = 842,000,000 x 2 bytes / step time.
 roofline: the compensate-quantize kernel's algorithmic bytes / its average launch time
@@ -35,7 +35,7 @@ TK_CHUNK, TK_K = 4096, 82
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard.json")
 CSRC = os.path.join(ROOT, "bit_gradient_compression_amd", "csrc")
 KERNEL_FILES = {"compensate_quantize_4bit": ["cq.hip"], "dequant_reduce_8peers": ["dr.hip"],
-                "sparseloco_topk_2bit": ["tk.hip"]}
+                "sparseloco_topk_2bit": ["tk.hip"], "sparseloco_aggregate_8peers": ["sa.hip"]}
 COMMON_FILES = ["loco_device.hpp", "loco_internal.hpp"]
 
 
@@ -60,6 +60,11 @@ def dr_bytes(n, peers, bits, block, out_bytes):
 def tk_bytes(n, chunk, k, bits):
     chunks = -(-n // chunk)
     return n * 12 + chunks * (2 * k + (k * bits + 7) // 8 + 4)
+
+
+def sa_bytes(n, peers, chunk, k, bits, out_bytes):
+    chunks = -(-n // chunk)
+    return peers * chunks * (2 * k + (k * bits + 7) // 8 + 4) + n * out_bytes
 
 
 def log(*a):
@@ -267,6 +272,19 @@ def main():
                                          "frac_hbm": round(bt / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                          "grad_GBps": round(nt * 4 / ms / 1e6, 1)}
         del gt, et, idx, tcodes, tabs
+        # SparseLoCo's sparse aggregation: 8 peers' Top-k payloads of the same shape into fp32 x 1/8
+        spays = [W.random_sparse_payload(nt, TK_CHUNK, TK_K, 2, key=("bench", p), device=dev) for p in range(PARTS)]
+        sout = torch.empty(nt, dtype=torch.float32, device=dev)
+        ms = timed(lambda: loco.loco_sparse_aggregate(spays, nt, chunk=TK_CHUNK, k=TK_K, bits=2, out=sout,
+                                                      out_scale=1.0 / PARTS, stream=stream),
+                   stream, max(3, args.steps // 3))
+        bs = sa_bytes(nt, PARTS, TK_CHUNK, TK_K, 2, 4)
+        modes["sparseloco_aggregate_8peers"] = {"workload": f"8 peers' Top-k payloads of {nt:,} (chunk 4096, k=82, "
+                                                            f"2-bit) into fp32 x 1/8",
+                                                "avg_ms": round(ms, 4), "alg_bytes": bs,
+                                                "GBps": round(bs / ms / 1e6, 1),
+                                                "frac_hbm": round(bs / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        del spays, sout
 
     cpu = None
     if args.cpu_sample > 0:

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libloco.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["abi.hip", "cq.hip", "dr.hip", "tk.hip"]
+SOURCES = ["abi.hip", "cq.hip", "dr.hip", "tk.hip", "sa.hip"]
 ARCH = "gfx950"
 
 

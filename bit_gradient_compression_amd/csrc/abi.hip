@@ -231,3 +231,47 @@ LOCO_API int loco_topk_quantize(const float* grad, float* err, int64_t n, int ch
     if (launch_tk(p, chunk, bits, (hipStream_t)stream) != hipSuccess) return LOCO_ERR_HIP;
     return LOCO_OK;
 }
+
+LOCO_API int loco_sparse_aggregate(const loco_sparse_payload_t* peers, int npeers, int64_t n, int chunk, int k,
+                                   int bits, float out_scale, void* out, loco_dtype_t out_dtype, void* stream) {
+    if (n < 0 || n > kMaxElems) return LOCO_ERR_INVALID;
+    if (npeers < 1 || !peers) return LOCO_ERR_INVALID;
+    if (npeers > kDrMaxPeers) return LOCO_ERR_UNSUPPORTED;
+    if (chunk <= 0 || chunk > 65536) return LOCO_ERR_INVALID;
+    if (k < 1 || k > chunk) return LOCO_ERR_INVALID;
+    if (bits < 1 || bits > 8) return LOCO_ERR_INVALID;
+    if (!bits_ok(bits)) return LOCO_ERR_UNSUPPORTED;
+    if (chunk != 256 && chunk != 512 && chunk != 1024 && chunk != 2048 && chunk != 4096)
+        return LOCO_ERR_UNSUPPORTED;
+    if (!isfinite(out_scale)) return LOCO_ERR_INVALID;
+    if (!dtype_ok(out_dtype)) return LOCO_ERR_INVALID;
+    if (n == 0) return LOCO_OK;
+    if (!out) return LOCO_ERR_INVALID;
+    if (!aligned16(out)) return LOCO_ERR_ALIGN;
+    const int64_t chunks = (n + chunk - 1) / chunk;
+    const Range ro = range_of(out, n * dtype_size(out_dtype));
+    for (int i = 0; i < npeers; ++i) {
+        const loco_sparse_payload_t& pe = peers[i];
+        if (!pe.idx || !pe.codes || !pe.absmax) return LOCO_ERR_INVALID;
+        if (!aligned16(pe.idx) || !aligned16(pe.codes) || !aligned16(pe.absmax)) return LOCO_ERR_ALIGN;
+        if (overlap(ro, range_of(pe.idx, chunks * k * 2)) || overlap(ro, range_of(pe.codes, chunks * code_bytes(k, bits))) ||
+            overlap(ro, range_of(pe.absmax, chunks * 4)))
+            return LOCO_ERR_INVALID;
+    }
+    SaParams p;
+    memset(&p, 0, sizeof(p));
+    for (int i = 0; i < npeers; ++i) {
+        p.peer[i].idx = peers[i].idx;
+        p.peer[i].codes = peers[i].codes;
+        p.peer[i].absmax = peers[i].absmax;
+    }
+    p.npeers = npeers;
+    p.k = k;
+    p.cbytes = (int)code_bytes(k, bits);
+    p.n = n;
+    p.nchunks = chunks;
+    p.out_scale = out_scale;
+    p.out = out;
+    if (launch_sa(p, chunk, bits, out_dtype == LOCO_BF16, (hipStream_t)stream) != hipSuccess) return LOCO_ERR_HIP;
+    return LOCO_OK;
+}

@@ -35,6 +35,9 @@ namespace loco {
 #ifndef LOCO_CQ_XCD_RUN
 #define LOCO_CQ_XCD_RUN 32
 #endif
+#ifndef LOCO_SA_XCD_RUN
+#define LOCO_SA_XCD_RUN 16
+#endif
 #ifndef LOCO_DR_XCD_RUN
 #define LOCO_DR_XCD_RUN 16
 #endif
@@ -49,6 +52,7 @@ constexpr int kXcds = 8;
 constexpr int kCqXcdRun = LOCO_CQ_XCD_RUN;
 constexpr int kCqXcdRunI8 = LOCO_CQ_XCD_RUN_I8;
 constexpr int kDrXcdRun = LOCO_DR_XCD_RUN;
+constexpr int kSaXcdRun = LOCO_SA_XCD_RUN;
 
 // Segments per launch; a call with more segments is split into several launches.
 constexpr int kCqMaxSeg = 32;
@@ -131,5 +135,36 @@ struct TkParams {
 };
 
 hipError_t launch_tk(const TkParams& p, int chunk, int bits, hipStream_t stream);
+
+// ---- sparse aggregation ------------------------------------------------------------
+
+#ifndef LOCO_SA_THREADS_F32
+#define LOCO_SA_THREADS_F32 256
+#endif
+#ifndef LOCO_SA_THREADS_BF16
+#define LOCO_SA_THREADS_BF16 128
+#endif
+constexpr int kSaThreadsF32 = LOCO_SA_THREADS_F32;    // threads per chunk, fp32 output
+constexpr int kSaThreadsBf16 = LOCO_SA_THREADS_BF16;  // threads per chunk, bf16 output
+constexpr int kSaPeerBatch = 8;    // peers whose first slot is loaded together
+
+struct SaPeerDev {
+    const uint16_t* idx;
+    const uint8_t* codes;
+    const float* absmax;
+};
+
+struct SaParams {
+    SaPeerDev peer[kDrMaxPeers];
+    int npeers;
+    int k;
+    int cbytes;  // code bytes per chunk, ceil(k*bits/8)
+    int64_t n;
+    int64_t nchunks;
+    float out_scale;
+    void* out;
+};
+
+hipError_t launch_sa(const SaParams& p, int chunk, int bits, bool out_bf16, hipStream_t stream);
 
 }  // namespace loco

@@ -26,7 +26,7 @@ LOCO_ERR_HIP = -4
 LOCO_MAX_PEERS = 128
 
 SYMBOLS = ["loco_compensate_quantize", "loco_compensate_quantize_ex", "loco_dequant_reduce",
-           "loco_topk_quantize", "loco_status_string", "loco_version"]
+           "loco_topk_quantize", "loco_sparse_aggregate", "loco_status_string", "loco_version"]
 
 
 class LocoError(RuntimeError):
@@ -48,6 +48,10 @@ class CqOptions(ctypes.Structure):
 
 class Payload(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
+
+
+class SparsePayload(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
 
 
 _lib = None
@@ -81,6 +85,10 @@ def load(path: str | None = None):
                                        ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.loco_topk_quantize.restype = ctypes.c_int
+    lib.loco_sparse_aggregate.argtypes = [ctypes.POINTER(SparsePayload), ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.loco_sparse_aggregate.restype = ctypes.c_int
     lib.loco_status_string.argtypes = [ctypes.c_int]
     lib.loco_status_string.restype = ctypes.c_char_p
     lib.loco_version.argtypes = []
@@ -199,8 +207,22 @@ def loco_topk_quantize(grad, err, *, chunk: int, k: int, idx, codes, absmax, bit
     _check("loco_topk_quantize", st)
 
 
+def loco_sparse_aggregate(peers, n: int, *, chunk: int, k: int, out, out_scale: float, bits: int = 2,
+                          stream=None) -> None:
+    """peers: iterable of (idx int16/uint16, codes uint8, absmax float32) tensors, as
+    loco_topk_quantize writes them."""
+    ps = list(peers)
+    arr = (SparsePayload * max(1, len(ps)))()
+    for i, (ix, c, a) in enumerate(ps):
+        arr[i] = SparsePayload(_ptr(ix), _ptr(c), _ptr(a))
+    st = load().loco_sparse_aggregate(arr if ps else None, len(ps), n, chunk, k, bits, out_scale, _ptr(out),
+                                      _dtype_code(out), _stream(stream))
+    _check("loco_sparse_aggregate", st)
+
+
 # short names
 compensate_quantize = loco_compensate_quantize
 compensate_quantize_ex = loco_compensate_quantize_ex
 dequant_reduce = loco_dequant_reduce
 topk_quantize = loco_topk_quantize
+sparse_aggregate = loco_sparse_aggregate

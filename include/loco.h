@@ -7,14 +7,16 @@
  *   Sec. 3.2 Eqns. (4)-(5) the moving-average compression error,
  *   Sec. 3.3 Eqn. (8) the all2all partitions and their high-precision average.
  *   "Communication Efficient LLM Pre-training with SparseLoCo" (summary and
- *   abstract): Top-k sparsification, 2-bit codes and error feedback.
+ *   abstract): Top-k sparsification, 2-bit codes and error feedback, and the sparse
+ *   aggregation of the nodes' sparse updates.
  *
  * The pages hand the method a flattened gradient (the FSDP communication hook) and
  * keep the error local to each node; the exchange between nodes is not part of this
  * library.  A rank calls loco_compensate_quantize on its flat gradient, split into
  * one segment per destination partition, sends each partition's payload
  * (codes + absmax) to its owner, and calls loco_dequant_reduce on the payloads it
- * receives.  loco_topk_quantize is the SparseLoCo-style mode.
+ * receives.  loco_topk_quantize is the SparseLoCo-style mode and loco_sparse_aggregate
+ * its receiving side.
  *
  * Conventions shared by every entry point
  *   - Device pointers are caller-owned device memory (e.g. PyTorch tensors) and must
@@ -192,6 +194,41 @@ int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_t n,
 int loco_topk_quantize(const float* grad, float* err, int64_t n, int chunk, int k,
                        int bits, float ef_decay, uint16_t* idx, uint8_t* codes,
                        float* absmax, void* stream);
+
+/* One peer's Top-k payload of a shard: what loco_topk_quantize wrote. */
+typedef struct {
+    const uint16_t* idx;   /* device u16[chunks * k] */
+    const uint8_t* codes;  /* device u8[chunks * ceil(k*bits/8)] */
+    const float* absmax;   /* device f32[chunks] */
+} loco_sparse_payload_t;
+
+/*
+ * loco_sparse_aggregate - SparseLoCo's sparse aggregation ("Communication Efficient LLM
+ * Pre-training with SparseLoCo", summary and abstract) of the peers' Top-k payloads of
+ * one shard into a dense output, computed as the high-precision average of LoCo
+ * Sec. 3.3, Eqn. (8) over sparse vectors.
+ *
+ * For every element i:
+ *   acc = 0;  for p = 0 .. npeers-1 in order: if peer p's chunk c = i / chunk has a
+ *   used slot j with idx_p[c*k + j] == i - c*chunk:  acc = acc + q_p[c, j] * step_p[c]
+ *   out[i] = acc * out_scale                      (out_scale = 1/N for the average)
+ * with step_p[c] = absmax_p[c] / qmax (0 for an all-zero chunk).  A slot is used when
+ * its index lies inside its chunk (the last chunk may be short); other slots, such as
+ * the 0xFFFF that loco_topk_quantize writes in unused slots, are skipped.  Elements no
+ * peer names are 0.  The slots of one peer's chunk must name distinct elements (as
+ * loco_topk_quantize writes them); repeated ones give an unspecified sum of their
+ * values but never touch memory outside the output.  The accumulator is fp32; bf16
+ * output rounds to nearest even.
+ *   peers      host array of npeers payloads, 1 <= npeers <= LOCO_MAX_PEERS
+ *   n          elements of the shard (>= 0; 0 is a no-op)
+ *   chunk      256, 512, 1024, 2048 or 4096;  1 <= k <= chunk;  bits 2, 4 or 8
+ *   out_scale  finite
+ *   out        device, n elements of out_dtype (written); must not overlap a payload
+ * where chunks = ceil(n / chunk).
+ */
+int loco_sparse_aggregate(const loco_sparse_payload_t* peers, int npeers, int64_t n,
+                          int chunk, int k, int bits, float out_scale, void* out,
+                          loco_dtype_t out_dtype, void* stream);
 
 /* A static, human-readable name for a status code. */
 const char* loco_status_string(int status);

@@ -57,6 +57,7 @@ __all__ = [
     "compensate_quantize",
     "cq_algorithmic_bytes", "block_steps", "dequant_reduce", "dr_algorithmic_bytes",
     "topk_order_select", "topk_quantize", "tk_algorithmic_bytes",
+    "sparse_aggregate", "sa_algorithmic_bytes",
 ]
 
 

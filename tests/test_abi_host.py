@@ -215,3 +215,37 @@ def test_cq_ex_int8_error_is_one_byte_per_element(lib):
     assert cqx(lib, [first, bad], ed=F32) == INV
     # and an overlap inside the int8 error's 1000 bytes is still refused
     assert cqx(lib, [seg(e=Bp, c=Bp + 992)]) == INV
+
+
+def spl(ix=Cp, c=Dp, a=0x70000000):
+    return loco.SparsePayload(ix, c, a)
+
+
+def sa(lib, peers, n=10000, chunk=4096, k=82, bits=2, scale=0.125, out=A, od=F32, npeers=None):
+    arr = (loco.SparsePayload * max(1, len(peers)))(*peers) if peers else None
+    return lib.loco_sparse_aggregate(arr, len(peers) if npeers is None else npeers, n, chunk, k, bits, scale,
+                                     out, od, None)
+
+
+@pytest.mark.parametrize("kwargs,want", [
+    (dict(npeers=0), INV), (dict(n=-1), INV), (dict(chunk=0), INV), (dict(chunk=70000), INV),
+    (dict(chunk=1000), UNSUP), (dict(chunk=8192), UNSUP), (dict(k=0), INV), (dict(k=4097), INV),
+    (dict(bits=3), UNSUP), (dict(bits=0), INV), (dict(scale=NAN), INV), (dict(scale=-math.inf), INV),
+    (dict(od=I8), INV), (dict(out=0), INV), (dict(out=A + 8), ALIGN),
+    (dict(out=Cp + 64), INV),             # output overlaps a peer's index array
+])
+def test_sa_checks(lib, kwargs, want):
+    assert sa(lib, [spl(), spl(Cp + 0x100000, Dp + 0x100000, 0x70100000)], **kwargs) == want
+
+
+def test_sa_peer_checks(lib):
+    assert sa(lib, [spl(ix=0)]) == INV
+    assert sa(lib, [spl(c=0)]) == INV
+    assert sa(lib, [spl(a=0)]) == INV
+    assert sa(lib, [spl(ix=Cp + 2)]) == ALIGN
+    assert sa(lib, [spl(a=0x70000000 + 4)]) == ALIGN
+    assert sa(lib, [spl()] * 129) == UNSUP
+    assert sa(lib, [], npeers=1) == INV
+    assert sa(lib, [spl()], n=0) == OK
+    # a peer's scales inside the last 16 bytes of the output
+    assert sa(lib, [spl(a=A + 10000 * 4 - 16)]) == INV

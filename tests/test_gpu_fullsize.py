@@ -165,3 +165,24 @@ def test_fullsize_sparseloco(gpu_lib):
             assert_f32_close(host(e[lo:hi]), ref["e_new"], np.full(C, float(ref["absmax"][0])), f"{t} error")
             ora_e[c] = ref["e_new"]
         del g
+
+
+def test_fullsize_sparse_aggregate(gpu_lib):
+    """8 peers' Top-k payloads of 2^28 (chunk 4096, k = 82, 2-bit) into fp32 x 1/8, as bench
+    launches it; sampled chunks against the oracle."""
+    n, C, k, bits, P = W.SPARSE_N, 4096, 82, 2, 8
+    cb = gpu_lib.code_bytes(k, bits)
+    say("sparse aggregate full: generating 8 payloads")
+    pays = [W.random_sparse_payload(n, C, k, bits, key=("full", p), device="cuda") for p in range(P)]
+    out = torch.empty(n, device="cuda")
+    gpu_lib.loco_sparse_aggregate(pays, n, chunk=C, k=k, bits=bits, out=out, out_scale=1.0 / P)
+    torch.cuda.synchronize()
+    chunks = n // C
+    rng = np.random.default_rng(11)
+    sample = sorted({0, chunks - 1} | set(int(x) for x in rng.integers(0, chunks, 64)))
+    for c in sample:
+        sl = [(host(ix[c * k:(c + 1) * k]).view(np.uint16), host(cd[c * cb:(c + 1) * cb]), host(a[c:c + 1]))
+              for ix, cd, a in pays]
+        want = oracle.sparse_aggregate(sl, C, chunk=C, k=k, bits=bits, out_scale=1.0 / P)
+        assert_f32_close(host(out[c * C:(c + 1) * C]), want, np.zeros(C), f"sparse aggregate chunk {c}")
+    say(f"sparse aggregate full: {len(sample)} chunks checked")

@@ -162,6 +162,31 @@ def random_payload(n, bits, block, key, device="cpu", zero_frac=0.1):
     return codes, absmax
 
 
+def random_sparse_payload(n, chunk, k, bits, key, device="cpu", zero_frac=0.1, drop_frac=0.02, ordered=True):
+    """A Top-k-shaped payload of n elements in chunks: per chunk, k distinct chunk-local
+    indices (ascending unless `ordered` is False); slots past a short last chunk's
+    length and a few dropped slots hold 0xFFFF.  Code bytes are uniformly random; the
+    per-chunk absmax is log-uniform in [1e-5, 1e-2], a fraction of them exactly zero.
+    The indices are an int16 tensor holding the u16 patterns."""
+    nch = -(-n // chunk)
+    g = _gen(device, "sparse-payload", key, n, chunk, k, bits)
+    r = torch.rand(nch, chunk, generator=g, device=device)
+    last = n - (nch - 1) * chunk
+    r[-1, last:] = -1.0  # positions past the end are picked only when k exceeds the length
+    idx = r.topk(k, dim=1).indices
+    if ordered:
+        idx = idx.sort(dim=1).values
+    unused = torch.rand(nch, k, generator=g, device=device) < drop_frac
+    unused[-1] |= idx[-1] >= last
+    idx = torch.where(unused, torch.full_like(idx, -1), idx).to(torch.int16)  # -1 is 0xFFFF
+    codes = torch.randint(0, 256, (nch * ((k * bits + 7) // 8),), generator=g, device=device,
+                          dtype=torch.int32).to(torch.uint8)
+    u = torch.rand(nch, generator=g, device=device, dtype=torch.float32)
+    absmax = torch.exp(math.log(1e-5) + u * (math.log(1e-2) - math.log(1e-5)))
+    absmax[torch.rand(nch, generator=g, device=device) < zero_frac] = 0.0
+    return idx.reshape(-1).contiguous(), codes, absmax
+
+
 # -- SparseLoCo pseudo-gradient -------------------------------------------------
 
 def sparseloco_grad(step, n=SPARSE_N, device="cpu", p_out=1e-3, sigma=1e-3):
