@@ -22,6 +22,10 @@ extracted text, so each step below is rebuilt from the prose around the equation
     - Sec. 3.3, Eqn. (8): the synchronised gradient is the average over the N nodes
       of the decompressed low-bit gradients, computed in high precision; with FSDP
       each node averages only its own partition (all2all, then a local average).
+    - Sec. 4, Eqn. (9): the Adam-family step on the synchronised gradient: moving
+      averages m (weight beta1 on the new gradient, m_0 = 0) and v (weight beta2 on
+      its square, v_0 = 0), the pre-conditioner 1 / sqrt(v + delta), and the update
+      of the weights by the learning rate times the pre-conditioned m.
 * "Communication Efficient LLM Pre-training with SparseLoCo" (summary and
   abstract): Top-k sparsification, 2-bit quantisation and error feedback, and a
   sparse aggregation of the nodes' sparse updates.
@@ -40,6 +44,9 @@ Readings where the pages are silent (each is also listed in the design notes):
 * SparseLoCo's sparse aggregation: the high-precision average of LoCo Eqn. (8)
   applied to the peers' sparse payloads (each scattered into a dense zero vector),
   accumulated in peer order.
+* LoCo-Adam (Eqn. (9)): m' = (1 - beta1) m + beta1 g (the v recursion is printed;
+  m follows it by analogy), no bias correction and no weight decay (the page names
+  neither), theta' = theta - lr * (m' * u) with u = 1 / sqrt(v' + delta).
 
 The functions are generic over the float type of their inputs: called with
 float32 arrays they are the parity oracle; called with float64 arrays they are
@@ -56,6 +63,7 @@ __all__ = [
     "error_update", "error_decompress", "error_compress", "pack_codes", "unpack_codes",
     "compensate_quantize",
     "cq_algorithmic_bytes", "block_steps", "dequant_reduce", "dr_algorithmic_bytes",
+    "adam_step", "dequant_reduce_adam", "dra_algorithmic_bytes",
     "topk_order_select", "topk_quantize", "tk_algorithmic_bytes",
     "sparse_aggregate", "sa_algorithmic_bytes",
 ]
@@ -304,6 +312,45 @@ def dequant_reduce(payloads, n, *, bits, block, out_scale, out_dtype="f32",
     if out_dtype == "bf16":
         return bf16_rne(out.astype(np.float32))
     return out
+
+
+def adam_step(theta, m, v, g, *, lr, beta1, beta2, delta, ftype=np.float32):
+    """LoCo Sec. 4, Eqn. (9), the Adam family with Adam's pre-conditioner, on the
+    synchronised gradient g:
+      m' = (1 - beta1) * m + beta1 * g
+      v' = (1 - beta2) * v + beta2 * (g * g)
+      u  = 1 / sqrt(v' + delta)
+      theta' = theta - lr * (m' * u)
+    Every operation is one IEEE rounding in the working type, in the order written
+    (1 - beta rounded first, as in error_update).  Returns (theta', m', v').
+    """
+    ft = ftype
+    theta, m, v, g = (np.asarray(x, dtype=ft) for x in (theta, m, v, g))
+    b1, b2 = ft(beta1), ft(beta2)
+    m_new = (ft(1) - b1) * m + b1 * g
+    v_new = (ft(1) - b2) * v + b2 * (g * g)
+    u = ft(1) / np.sqrt(v_new + ft(delta))
+    theta_new = theta - ft(lr) * (m_new * u)
+    return theta_new, m_new, v_new
+
+
+def dequant_reduce_adam(payloads, n, *, bits, block, out_scale, theta, m, v, lr, beta1, beta2, delta,
+                        fixed_scale=0.0, ftype=np.float32):
+    """Eqn. (8) then Eqn. (9) on one partition: the peers' payloads are averaged in
+    high precision (dequant_reduce, fp32, never rounded to bf16) and the result is the
+    gradient of one Adam-family step.  Returns dict(theta, m, v, g, theta_bf16) with
+    theta_bf16 the RNE bf16 copy of the new weights."""
+    g = dequant_reduce(payloads, n, bits=bits, block=block, out_scale=out_scale, out_dtype="f32",
+                       fixed_scale=fixed_scale, ftype=ftype)
+    theta_new, m_new, v_new = adam_step(theta, m, v, g, lr=lr, beta1=beta1, beta2=beta2, delta=delta,
+                                        ftype=ftype)
+    return {"theta": theta_new, "m": m_new, "v": v_new, "g": g,
+            "theta_bf16": bf16_rne(np.asarray(theta_new, np.float32))}
+
+
+def dra_algorithmic_bytes(n, npeers, bits, block, param_bf16=False, fixed_scale=False):
+    """Peer payloads read once; theta, m, v (fp32) read and written; optional bf16 copy."""
+    return dr_algorithmic_bytes(n, npeers, bits, block, 0, fixed_scale) + 24 * n + (2 * n if param_bf16 else 0)
 
 
 def dr_algorithmic_bytes(n, npeers, bits, block, out_bytes, fixed_scale=False):

@@ -95,3 +95,12 @@ def sa_case():
         else:
             d[k] = int(rest)
     return d
+
+
+def adam_case():
+    d = {}
+    for ln in _lines("adam_worked.txt"):
+        k, rest = ln.split(None, 1)
+        v = rest.split()
+        d[k] = float(v[0]) if len(v) == 1 and k in ("lr", "beta1", "beta2", "delta") else np.array(v, np.float32)
+    return d

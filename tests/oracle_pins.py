@@ -534,6 +534,58 @@ def pin_sa_transmits_topk(O):
         assert not np.any(out[~kept])
 
 
+# -- LoCo-Adam on the synchronised gradient (LoCo Sec. 4, Eqn. (9)) --------------------------------
+
+def pin_adam_worked(O):
+    c = golden_io.adam_case()
+    th, m, v = O.adam_step(c["theta"], c["m"], c["v"], c["g"], lr=c["lr"], beta1=c["beta1"], beta2=c["beta2"],
+                           delta=c["delta"])
+    assert np.array_equal(m, c["m_new"]), (m, c["m_new"])
+    assert np.array_equal(v, c["v_new"]), (v, c["v_new"])
+    assert np.array_equal(th, c["theta_new"]), (th, c["theta_new"])
+    tb = torch.from_numpy(th).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(tb, th)  # the worked weights are exact in bf16 too
+
+
+def pin_adam_closed_form(O):
+    """A constant gradient from m_0 = v_0 = 0: m_k = (1 - (1 - b1)^k) g and
+    v_k = (1 - (1 - b2)^k) g^2, so theta_K = theta_0 - lr * sum_k m_k / sqrt(v_k + delta)
+    (float64 twin, to rounding)."""
+    rng = _rng(40)
+    n, K, lr, b1, b2, delta = 500, 30, 1e-3, 0.1, 0.02, 1e-8
+    g = rng.standard_normal(n) * 1e-3
+    th0 = rng.standard_normal(n)
+    th, m, v = th0.copy(), np.zeros(n), np.zeros(n)
+    want = th0.copy()
+    for k in range(1, K + 1):
+        th, m, v = O.adam_step(th, m, v, g, lr=lr, beta1=b1, beta2=b2, delta=delta, ftype=np.float64)
+        mk = (1 - (1 - b1) ** k) * g
+        vk = (1 - (1 - b2) ** k) * g * g
+        assert np.allclose(m, mk, rtol=1e-12, atol=0) and np.allclose(v, vk, rtol=1e-12, atol=0)
+        want = want - lr * mk / np.sqrt(vk + delta)
+    assert np.allclose(th, want, rtol=1e-12, atol=1e-15)
+
+
+def pin_adam_limits(O):
+    """beta1 = beta2 = 1 with a tiny delta is sign descent: theta moves by lr * sign(g) to a
+    few ulp; lr = 0 leaves theta bitwise; a zero gradient only decays m and v."""
+    rng = _rng(41)
+    n = 4000
+    g = (rng.standard_normal(n) * 10.0 ** rng.integers(-6, 1, n)).astype(F32)
+    th = rng.standard_normal(n).astype(F32)
+    m = rng.standard_normal(n).astype(F32)
+    v = (rng.random(n) * 1e-4).astype(F32)
+    t1, m1, v1 = O.adam_step(th, m, v, g, lr=2.0 ** -10, beta1=1.0, beta2=1.0, delta=2.0 ** -120)
+    assert np.array_equal(m1, g) and np.array_equal(v1, g * g)
+    step = (th.astype(np.float64) - t1.astype(np.float64)) / 2.0 ** -10
+    slack = 8 * np.spacing(np.abs(th)).astype(np.float64) / 2.0 ** -10 + 4 * 2.0 ** -23
+    assert np.all(np.abs(step - np.sign(g)) <= slack)
+    t2, _, _ = O.adam_step(th, m, v, g, lr=0.0, beta1=0.1, beta2=0.01, delta=1e-8)
+    assert np.array_equal(t2, th)
+    _, m3, v3 = O.adam_step(th, m, v, np.zeros(n, F32), lr=1e-3, beta1=0.1, beta2=0.01, delta=1e-8)
+    assert np.array_equal(m3, (F32(1) - F32(0.1)) * m) and np.array_equal(v3, (F32(1) - F32(0.01)) * v)
+
+
 ALL_PINS = [
     pin_identity_compressor, pin_beta_zero_is_efc, pin_quantisation_bound,
     pin_random_walk_bounded, pin_telescoping, pin_fixed_scale_golden, pin_torch_quantiser,
@@ -541,4 +593,5 @@ ALL_PINS = [
     pin_dequant_reduce, pin_zero_blocks, pin_bf16_rne, pin_topk_error_feedback,
     pin_i8_error_accounting, pin_i8_equals_float_when_exact, pin_reset, pin_i8_compressor_vs_torch,
     pin_sa_worked, pin_sa_brute_force, pin_sa_dense_equivalent, pin_sa_transmits_topk,
+    pin_adam_worked, pin_adam_closed_form, pin_adam_limits,
 ]

@@ -144,6 +144,27 @@ def _sa_slot_scale(payloads, n, **kw):
     return _orig["sparse_aggregate"](out, n, **kw)
 
 
+def _adam_swapped(theta, m, v, g, *, lr, beta1, beta2, delta, ftype=np.float32):
+    return _orig["adam_step"](theta, m, v, g, lr=lr, beta1=1 - beta1, beta2=beta2, delta=delta, ftype=ftype)
+
+
+def _adam_delta_outside(theta, m, v, g, *, lr, beta1, beta2, delta, ftype=np.float32):
+    ft = ftype
+    theta, m, v, g = (np.asarray(x, dtype=ft) for x in (theta, m, v, g))
+    m_new = (ft(1) - ft(beta1)) * m + ft(beta1) * g
+    v_new = (ft(1) - ft(beta2)) * v + ft(beta2) * (g * g)
+    return theta - ft(lr) * (m_new / (np.sqrt(v_new) + ft(delta))), m_new, v_new
+
+
+def _adam_bias_corrected(theta, m, v, g, *, lr, beta1, beta2, delta, ftype=np.float32):
+    ft = ftype
+    theta, m, v, g = (np.asarray(x, dtype=ft) for x in (theta, m, v, g))
+    m_new = (ft(1) - ft(beta1)) * m + ft(beta1) * g
+    v_new = (ft(1) - ft(beta2)) * v + ft(beta2) * (g * g)
+    mh, vh = m_new / ft(beta1), v_new / ft(beta2)  # first-step bias correction
+    return theta - ft(lr) * (mh / np.sqrt(vh + ft(delta))), m_new, v_new
+
+
 MUTATIONS = {
     "error_update drops beta*e": ("error_update", _drop_beta_term),
     "error_update swaps beta and 1-beta": ("error_update", _swap_weights),
@@ -166,6 +187,9 @@ MUTATIONS = {
     "sparse aggregation without out_scale": ("sparse_aggregate", _sa_no_scale),
     "sparse aggregation index off by one": ("sparse_aggregate", _sa_index_plus_one),
     "sparse aggregation with the first chunk's scale": ("sparse_aggregate", _sa_slot_scale),
+    "Adam with beta1 weighting the old moment": ("adam_step", _adam_swapped),
+    "Adam with delta outside the square root": ("adam_step", _adam_delta_outside),
+    "Adam with bias correction": ("adam_step", _adam_bias_corrected),
 }
 
 
