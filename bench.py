@@ -7,8 +7,9 @@ A step is one pass of the rank's path on the 7B FSDP-shard workload:
   dequant-reduce of the 8 peer payloads of the rank's own partition into bf16 (x 1/8).
 Inputs are resident in HBM before the timed region; the error buffer carries over from
 step to step.  The SparseLoCo-style Top-k mode (2^28 fp32, chunk 4096, k = 82, 2-bit),
-its sparse aggregation of 8 peers' payloads, the 8-bit-code variant and the 8-bit-error
-variant (LoCo Eqn. (7)) are timed in the same run and reported under "modes".
+its sparse aggregation of 8 peers' payloads, the 8-bit-code variant, the 8-bit-error
+variant (LoCo Eqn. (7)) and dequant-reduce fused with the LoCo-Adam step (Eqn. (9)) are
+timed in the same run and reported under "modes".
 
 Prints one JSON line.  value = gradient GB/s = 842,000,000 x 2 bytes / step time.
 roofline: the compensate-quantize kernel's algorithmic bytes / its average launch time
@@ -35,6 +36,7 @@ TK_CHUNK, TK_K = 4096, 82
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard.json")
 CSRC = os.path.join(ROOT, "bit_gradient_compression_amd", "csrc")
 KERNEL_FILES = {"compensate_quantize_4bit": ["cq.hip"], "dequant_reduce_8peers": ["dr.hip"],
+                "dequant_reduce_adam_8peers": ["dr.hip"],
                 "sparseloco_topk_2bit": ["tk.hip"], "sparseloco_aggregate_8peers": ["sa.hip"]}
 COMMON_FILES = ["loco_device.hpp", "loco_internal.hpp"]
 
@@ -254,6 +256,23 @@ def main():
                                                             "grad_GBps": round(n * 2 / ms / 1e6, 1),
                                                             "err_scale": 2.0 ** 17}
         del ei8, segs_i8
+        # the partition's payloads averaged straight into one LoCo-Adam step (Eqns. (8)-(9)):
+        # fp32 weights and moments updated in place, plus the bf16 weight copy
+        th = torch.randn(part, device=dev) * 0.02
+        m_ = torch.zeros(part, device=dev)
+        v_ = torch.zeros(part, device=dev)
+        tb = torch.empty(part, dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda: loco.loco_dequant_reduce_adam(payloads, part, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS,
+                                                         param=th, m=m_, v=v_, lr=1e-4, beta1=0.1, beta2=0.01,
+                                                         delta=1e-8, param_bf16=tb, stream=stream),
+                   stream, max(3, args.steps // 3))
+        bda = dr_bytes(part, PARTS, BITS, BLOCK, 0) + 26 * part
+        modes["dequant_reduce_adam_8peers"] = {"workload": f"8 peer 4-bit payloads of {part:,} averaged into one "
+                                                           "Adam step (fp32 weights, m, v; bf16 weight copy)",
+                                               "avg_ms": round(ms, 4), "alg_bytes": bda,
+                                               "GBps": round(bda / ms / 1e6, 1),
+                                               "frac_hbm": round(bda / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        del th, m_, v_, tb
         # SparseLoCo-style mode on its own workload
         nt = W.SPARSE_N
         gt = W.sparseloco_grad(0, n=nt, device=dev)

@@ -155,9 +155,11 @@ LOCO_API int loco_compensate_quantize_ex(const loco_cq_segment_t* segs, int nseg
     return compensate_quantize(segs, nseg, grad_dtype, err_dtype, *opt, (hipStream_t)stream);
 }
 
-LOCO_API int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_t n, int bits,
-                                 int block, float fixed_scale, float out_scale, void* out,
-                                 loco_dtype_t out_dtype, void* stream) {
+namespace {
+
+// Checks shared by both dequant-reduce entry points; fills the payload part of p.
+int dr_setup(const loco_payload_t* peers, int npeers, int64_t n, int bits, int block, float fixed_scale,
+             float out_scale, DrParams& p, bool& fixed) {
     if (n < 0 || n > kMaxElems) return LOCO_ERR_INVALID;
     if (npeers < 1 || !peers) return LOCO_ERR_INVALID;
     if (npeers > kDrMaxPeers) return LOCO_ERR_UNSUPPORTED;
@@ -165,36 +167,91 @@ LOCO_API int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_
     if (!bits_ok(bits)) return LOCO_ERR_UNSUPPORTED;
     if (!isfinite(fixed_scale) || fixed_scale < 0.0f) return LOCO_ERR_INVALID;
     if (!isfinite(out_scale)) return LOCO_ERR_INVALID;
-    if (!dtype_ok(out_dtype)) return LOCO_ERR_INVALID;
-    const bool fixed = fixed_scale > 0.0f;
+    fixed = fixed_scale > 0.0f;
     if (!fixed) {
         if (block <= 0) return LOCO_ERR_INVALID;
         if (!block_ok(block)) return LOCO_ERR_UNSUPPORTED;
     }
-    if (n == 0) return LOCO_OK;
-    if (!out) return LOCO_ERR_INVALID;
-    if (!aligned16(out)) return LOCO_ERR_ALIGN;
-    const Range ro = range_of(out, n * dtype_size(out_dtype));
+    memset(&p, 0, sizeof(p));
     for (int i = 0; i < npeers; ++i) {
         if (!peers[i].codes || (!fixed && !peers[i].absmax)) return LOCO_ERR_INVALID;
         if (!aligned16(peers[i].codes) || (!fixed && !aligned16(peers[i].absmax))) return LOCO_ERR_ALIGN;
-        if (overlap(ro, range_of(peers[i].codes, code_bytes(n, bits)))) return LOCO_ERR_INVALID;
-        if (!fixed && overlap(ro, range_of(peers[i].absmax, nblocks(n, block) * 4))) return LOCO_ERR_INVALID;
-    }
-    DrParams p;
-    memset(&p, 0, sizeof(p));
-    for (int i = 0; i < npeers; ++i) {
         p.peer[i].codes = peers[i].codes;
         p.peer[i].absmax = peers[i].absmax;
     }
     p.npeers = npeers;
     p.n = n;
-    p.ntiles = (n + kDrTile - 1) / kDrTile;
     p.fixed_step = fixed ? 1.0f / fixed_scale : 0.0f;
     p.out_scale = out_scale;
+    return LOCO_OK;
+}
+
+// An output range must not overlap any peer's payload.
+bool overlaps_payloads(const loco_payload_t* peers, int npeers, int64_t n, int bits, int block, bool fixed, Range r) {
+    for (int i = 0; i < npeers; ++i) {
+        if (overlap(r, range_of(peers[i].codes, code_bytes(n, bits)))) return true;
+        if (!fixed && overlap(r, range_of(peers[i].absmax, nblocks(n, block) * 4))) return true;
+    }
+    return false;
+}
+
+}  // namespace
+
+LOCO_API int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_t n, int bits,
+                                 int block, float fixed_scale, float out_scale, void* out,
+                                 loco_dtype_t out_dtype, void* stream) {
+    DrParams p;
+    bool fixed = false;
+    const int st = dr_setup(peers, npeers, n, bits, block, fixed_scale, out_scale, p, fixed);
+    if (st != LOCO_OK) return st;
+    if (!dtype_ok(out_dtype)) return LOCO_ERR_INVALID;
+    if (n == 0) return LOCO_OK;
+    if (!out) return LOCO_ERR_INVALID;
+    if (!aligned16(out)) return LOCO_ERR_ALIGN;
+    if (overlaps_payloads(peers, npeers, n, bits, block, fixed, range_of(out, n * dtype_size(out_dtype))))
+        return LOCO_ERR_INVALID;
+    const int mode = out_dtype == LOCO_BF16 ? kDrOutBf16 : kDrOutF32;
+    p.ntiles = (n + dr_tile_elems(mode) - 1) / dr_tile_elems(mode);
     p.out = out;
-    if (launch_dr(p, bits, block, fixed, out_dtype == LOCO_BF16, (hipStream_t)stream) != hipSuccess)
-        return LOCO_ERR_HIP;
+    if (launch_dr(p, bits, block, fixed, mode, (hipStream_t)stream) != hipSuccess) return LOCO_ERR_HIP;
+    return LOCO_OK;
+}
+
+LOCO_API int loco_dequant_reduce_adam(const loco_payload_t* peers, int npeers, int64_t n, int bits, int block,
+                                      float fixed_scale, float out_scale, const loco_adam_t* adam, float* param,
+                                      float* m, float* v, uint16_t* param_bf16, void* stream) {
+    DrParams p;
+    bool fixed = false;
+    const int st = dr_setup(peers, npeers, n, bits, block, fixed_scale, out_scale, p, fixed);
+    if (st != LOCO_OK) return st;
+    if (!adam) return LOCO_ERR_INVALID;
+    const loco_adam_t& a = *adam;
+    if (!isfinite(a.lr) || !isfinite(a.beta1) || !isfinite(a.beta2) || !isfinite(a.delta)) return LOCO_ERR_INVALID;
+    if (a.beta1 < 0.0f || a.beta1 > 1.0f || a.beta2 < 0.0f || a.beta2 > 1.0f || !(a.delta > 0.0f))
+        return LOCO_ERR_INVALID;
+    if (n == 0) return LOCO_OK;
+    if (!param || !m || !v) return LOCO_ERR_INVALID;
+    if (!aligned16(param) || !aligned16(m) || !aligned16(v) || (param_bf16 && !aligned16(param_bf16)))
+        return LOCO_ERR_ALIGN;
+    Range r[4] = {range_of(param, n * 4), range_of(m, n * 4), range_of(v, n * 4),
+                  range_of(param_bf16, param_bf16 ? n * 2 : 0)};
+    for (int x = 0; x < 4; ++x) {
+        for (int y = x + 1; y < 4; ++y)
+            if (overlap(r[x], r[y])) return LOCO_ERR_INVALID;
+        if (overlaps_payloads(peers, npeers, n, bits, block, fixed, r[x])) return LOCO_ERR_INVALID;
+    }
+    p.ntiles = (n + dr_tile_elems(kDrOutAdam) - 1) / dr_tile_elems(kDrOutAdam);
+    p.theta = param;
+    p.m = m;
+    p.v = v;
+    p.theta_bf16 = param_bf16;
+    p.lr = a.lr;
+    p.beta1 = a.beta1;
+    p.omb1 = 1.0f - a.beta1;
+    p.beta2 = a.beta2;
+    p.omb2 = 1.0f - a.beta2;
+    p.delta = a.delta;
+    if (launch_dr(p, bits, block, fixed, kDrOutAdam, (hipStream_t)stream) != hipSuccess) return LOCO_ERR_HIP;
     return LOCO_OK;
 }
 

@@ -11,6 +11,13 @@
 // written lines are whole.  The 8 outputs of a lane sit in one scale block (blocks are
 // >= 64 elements).  The fp32 accumulator never leaves registers; only the reduced shard
 // is written.  One wave tile per wave, the grid covering all tiles.
+//
+// Fused consumer (LoCo, Sec. 4, Eqn. (9)): instead of writing the reduced gradient g,
+// the kernel takes one Adam-family step with it on the partition's fp32 weights and
+// moments, which it reads and writes in the same pass:
+//   m' = (1-b1) m + b1 g;  v' = (1-b2) v + b2 g^2;  u = 1 / sqrt(v' + delta)
+//   theta' = theta - lr (m' u)
+// and optionally writes a bf16 copy of theta'.  The reduced gradient never reaches HBM.
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"
@@ -83,9 +90,9 @@ __device__ __forceinline__ float peer_step(const DrPeerDev& pe, int64_t i0, floa
     else return pe.absmax[i0 / B] / (float)QMAX;  // 0 for an all-zero block
 }
 
-template <bool OBF>
+template <int MODE>
 __device__ __forceinline__ void store_out8(void* out, int64_t i0, const float (&acc)[kDrVec], float scale) {
-    if constexpr (OBF) {
+    if constexpr (MODE == kDrOutBf16) {
         u32x4 s;
         s.x = bf16x2_rne(acc[0] * scale, acc[1] * scale);
         s.y = bf16x2_rne(acc[2] * scale, acc[3] * scale);
@@ -101,44 +108,80 @@ __device__ __forceinline__ void store_out8(void* out, int64_t i0, const float (&
     }
 }
 
-template <int BITS, int B, bool FIXED, bool OBF>
+// The Adam-family step on one element (Eqn. (9)), in the oracle's order of roundings.
+__device__ __forceinline__ void adam1(const DrParams& p, float g, float& th, float& m, float& v) {
+    m = p.omb1 * m + p.beta1 * g;
+    v = p.omb2 * v + p.beta2 * (g * g);
+    const float u = 1.0f / sqrtf(v + p.delta);
+    th = th - p.lr * (m * u);
+}
+
+__device__ __forceinline__ void load8f(const float* src, int64_t i0, float (&x)[kDrVec]) {
+    const f32x4* q = (const f32x4*)(src + i0);
+    const f32x4 a = q[0], b = q[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store8f(float* dst, int64_t i0, const float (&x)[kDrVec]) {
+    f32x4* q = (f32x4*)(dst + i0);
+    f32x4 a = {x[0], x[1], x[2], x[3]};
+    f32x4 b = {x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(a, q);
+    __builtin_nontemporal_store(b, q + 1);
+}
+
+template <int BITS, int B, bool FIXED, int MODE>
 __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
-    static_assert(kDrTile % B == 0, "a wave tile spans whole scale blocks");
+    constexpr int U = dr_unroll(MODE);
+    constexpr int TILE = dr_tile_elems(MODE);
+    constexpr bool ADAM = MODE == kDrOutAdam;
+    static_assert(TILE % B == 0, "a wave tile spans whole scale blocks");
     constexpr int SUB = 64 * kDrVec;
     const int lane = lane_id();
     const int64_t nwaves = (int64_t)gridDim.x * (kDrThreads / kWave);
     const int64_t wg = xcd_remap<kXcds, kDrXcdRun>(blockIdx.x, gridDim.x);
     for (int64_t t = wg * (kDrThreads / kWave) + uniform(threadIdx.x / kWave); t < p.ntiles;
          t += nwaves) {
-        const int64_t base = t * kDrTile + lane * kDrVec;
-        float acc[kDrUnroll][kDrVec];
+        const int64_t base = t * TILE + lane * kDrVec;
+        float acc[U][kDrVec];
 #pragma unroll
-        for (int u = 0; u < kDrUnroll; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < kDrVec; ++j) acc[u][j] = 0.0f;
 
-        if ((t + 1) * kDrTile <= p.n) {
+        if ((t + 1) * TILE <= p.n) {
+            // The optimizer state is loaded first, so its latency overlaps the payloads'.
+            float th[ADAM ? U : 1][kDrVec], mo[ADAM ? U : 1][kDrVec], ve[ADAM ? U : 1][kDrVec];
+            if constexpr (ADAM) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    load8f(p.theta, base + u * SUB, th[u]);
+                    load8f(p.m, base + u * SUB, mo[u]);
+                    load8f(p.v, base + u * SUB, ve[u]);
+                }
+            }
             // whole wave tile in range.  The tile spans BPT scale blocks; the steps of G
             // peers x BPT blocks are computed one per lane (one division per lane per G
             // peers) and each lane fetches its block's step with a lane shuffle.
-            constexpr int BPT = kDrTile / B;
+            constexpr int BPT = TILE / B;
             constexpr int G = 64 / BPT;
-            const int64_t blk0 = t * (kDrTile / B);
-            int myblk[kDrUnroll];
+            const int64_t blk0 = t * (TILE / B);
+            int myblk[U];
 #pragma unroll
-            for (int u = 0; u < kDrUnroll; ++u) myblk[u] = (int)((base + u * SUB) / B - blk0);
+            for (int u = 0; u < U; ++u) myblk[u] = (int)((base + u * SUB) / B - blk0);
             for (int pg = 0; pg < p.npeers; pg += G) {
                 const int ng = p.npeers - pg < G ? p.npeers - pg : G;
                 // codes of a batch of peers, all loads in flight together (slots past the
                 // group re-read its last peer and are not accumulated)
-                u32x2 w[kDrPeerBatch][kDrUnroll];
+                u32x2 w[kDrPeerBatch][U];
                 auto load_batch = [&](int q0) {
 #pragma unroll
                     for (int b = 0; b < kDrPeerBatch; ++b) {
                         const int q = q0 + b < ng ? q0 + b : ng - 1;
                         const uint8_t* codes = p.peer[pg + q].codes;
 #pragma unroll
-                        for (int u = 0; u < kDrUnroll; ++u) w[b][u] = load_codes8<BITS>(codes, base + u * SUB);
+                        for (int u = 0; u < U; ++u) w[b][u] = load_codes8<BITS>(codes, base + u * SUB);
                     }
                 };
                 load_batch(0);  // issued before the scales, so both latencies overlap
@@ -163,7 +206,7 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                     for (int b = 0; b < kDrPeerBatch; ++b) {
                         if (q0 + b < ng) {
 #pragma unroll
-                            for (int u = 0; u < kDrUnroll; ++u) {
+                            for (int u = 0; u < U; ++u) {
                                 const float step = FIXED ? stp : __shfl(stp, (q0 + b) * BPT + myblk[u], 64);
                                 accumulate8<BITS>(acc[u], w[b][u], step);
                             }
@@ -171,12 +214,31 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                     }
                 }
             }
+            if constexpr (ADAM) {
 #pragma unroll
-            for (int u = 0; u < kDrUnroll; ++u) store_out8<OBF>(p.out, base + u * SUB, acc[u], p.out_scale);
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int j = 0; j < kDrVec; ++j) adam1(p, acc[u][j] * p.out_scale, th[u][j], mo[u][j], ve[u][j]);
+                    store8f(p.theta, base + u * SUB, th[u]);
+                    store8f(p.m, base + u * SUB, mo[u]);
+                    store8f(p.v, base + u * SUB, ve[u]);
+                    if (p.theta_bf16) {
+                        u32x4 s;
+                        s.x = bf16x2_rne(th[u][0], th[u][1]);
+                        s.y = bf16x2_rne(th[u][2], th[u][3]);
+                        s.z = bf16x2_rne(th[u][4], th[u][5]);
+                        s.w = bf16x2_rne(th[u][6], th[u][7]);
+                        __builtin_nontemporal_store(s, (u32x4*)(p.theta_bf16 + base + u * SUB));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) store_out8<MODE>(p.out, base + u * SUB, acc[u], p.out_scale);
+            }
         } else {
             // ragged tail: element-wise, reading only the bytes that exist
 #pragma unroll
-            for (int u = 0; u < kDrUnroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int64_t i0 = base + u * SUB;
                 const int64_t left = p.n - i0;
                 const int nvalid = left <= 0 ? 0 : (left >= kDrVec ? kDrVec : (int)left);
@@ -197,9 +259,20 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
 #pragma unroll
                 for (int j = 0; j < kDrVec; ++j) {
                     if (j < nvalid) {
-                        const float v = acc[u][j] * p.out_scale;
-                        if constexpr (OBF) ((uint16_t*)p.out)[i0 + j] = bf16_rne(v);
-                        else ((float*)p.out)[i0 + j] = v;
+                        const float g = acc[u][j] * p.out_scale;
+                        if constexpr (ADAM) {
+                            const int64_t i = i0 + j;
+                            float th1 = p.theta[i], m1 = p.m[i], v1 = p.v[i];
+                            adam1(p, g, th1, m1, v1);
+                            p.theta[i] = th1;
+                            p.m[i] = m1;
+                            p.v[i] = v1;
+                            if (p.theta_bf16) p.theta_bf16[i] = bf16_rne(th1);
+                        } else if constexpr (MODE == kDrOutBf16) {
+                            ((uint16_t*)p.out)[i0 + j] = bf16_rne(g);
+                        } else {
+                            ((float*)p.out)[i0 + j] = g;
+                        }
                     }
                 }
             }
@@ -207,38 +280,45 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
     }
 }
 
-template <int BITS, bool FIXED, bool OBF>
+template <int BITS, bool FIXED, int MODE>
 const void* pick_block(int block) {
     if constexpr (FIXED) {
-        return (const void*)&dr_kernel<BITS, 64, true, OBF>;
+        return (const void*)&dr_kernel<BITS, 64, true, MODE>;
     } else {
         switch (block) {
-            case 64: return (const void*)&dr_kernel<BITS, 64, false, OBF>;
-            case 128: return (const void*)&dr_kernel<BITS, 128, false, OBF>;
-            case 256: return (const void*)&dr_kernel<BITS, 256, false, OBF>;
-            case 512: return (const void*)&dr_kernel<BITS, 512, false, OBF>;
+            case 64: return (const void*)&dr_kernel<BITS, 64, false, MODE>;
+            case 128: return (const void*)&dr_kernel<BITS, 128, false, MODE>;
+            case 256: return (const void*)&dr_kernel<BITS, 256, false, MODE>;
+            case 512: return (const void*)&dr_kernel<BITS, 512, false, MODE>;
         }
         return nullptr;
     }
 }
 
-template <bool FIXED, bool OBF>
+template <bool FIXED, int MODE>
 const void* pick_bits(int bits, int block) {
     switch (bits) {
-        case 2: return pick_block<2, FIXED, OBF>(block);
-        case 4: return pick_block<4, FIXED, OBF>(block);
-        case 8: return pick_block<8, FIXED, OBF>(block);
+        case 2: return pick_block<2, FIXED, MODE>(block);
+        case 4: return pick_block<4, FIXED, MODE>(block);
+        case 8: return pick_block<8, FIXED, MODE>(block);
     }
     return nullptr;
 }
 
+template <int MODE>
+const void* pick_fixed(bool fixed, int bits, int block) {
+    return fixed ? pick_bits<true, MODE>(bits, block) : pick_bits<false, MODE>(bits, block);
+}
+
 }  // namespace
 
-hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, bool out_bf16,
-                     hipStream_t stream) {
+hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, int mode, hipStream_t stream) {
     const void* k = nullptr;
-    if (fixed) k = out_bf16 ? pick_bits<true, true>(bits, block) : pick_bits<true, false>(bits, block);
-    else k = out_bf16 ? pick_bits<false, true>(bits, block) : pick_bits<false, false>(bits, block);
+    switch (mode) {
+        case kDrOutF32: k = pick_fixed<kDrOutF32>(fixed, bits, block); break;
+        case kDrOutBf16: k = pick_fixed<kDrOutBf16>(fixed, bits, block); break;
+        case kDrOutAdam: k = pick_fixed<kDrOutAdam>(fixed, bits, block); break;
+    }
     if (!k) return hipErrorInvalidValue;
     const int64_t waves_per_block = kDrThreads / kWave;
     int64_t blocks = (p.ntiles + waves_per_block - 1) / waves_per_block;

@@ -94,8 +94,17 @@ hipError_t launch_cq(const CqParams& p, int grad_kind, int err_kind, int bits, i
 constexpr int kDrMaxPeers = 128;
 constexpr int kDrVec = 8;                          // consecutive outputs per lane per sub-tile
 constexpr int kDrUnroll = LOCO_DR_UNROLL;          // sub-tiles per wave tile
-constexpr int kDrTile = 64 * kDrVec * kDrUnroll;   // elements per wave tile
 constexpr int kDrThreads = LOCO_DR_THREADS;
+// Output modes: the reduced shard as fp32 or bf16, or the fused Adam-family step.
+enum : int { kDrOutF32 = 0, kDrOutBf16 = 1, kDrOutAdam = 2 };
+// The fused step holds theta, m and v of each sub-tile in registers as well, so its waves
+// take one sub-tile.
+#ifndef LOCO_DRA_UNROLL
+#define LOCO_DRA_UNROLL 1
+#endif
+constexpr int kDrUnrollAdam = LOCO_DRA_UNROLL;
+constexpr int dr_unroll(int mode) { return mode == kDrOutAdam ? kDrUnrollAdam : kDrUnroll; }
+constexpr int dr_tile_elems(int mode) { return 64 * kDrVec * dr_unroll(mode); }  // per wave tile
 constexpr int kDrPeerBatch = 8;                    // peers whose codes are loaded together
 
 struct DrPeerDev {
@@ -111,10 +120,15 @@ struct DrParams {
     float fixed_step;
     float out_scale;
     void* out;
+    // fused Adam-family step (mode kDrOutAdam)
+    float* theta;
+    float* m;
+    float* v;
+    uint16_t* theta_bf16;  // may be null
+    float lr, beta1, omb1, beta2, omb2, delta;  // omb = fl(1 - beta)
 };
 
-hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, bool out_bf16,
-                     hipStream_t stream);
+hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, int mode, hipStream_t stream);
 
 // ---- chunked Top-k ----------------------------------------------------------------
 

@@ -26,7 +26,8 @@ LOCO_ERR_HIP = -4
 LOCO_MAX_PEERS = 128
 
 SYMBOLS = ["loco_compensate_quantize", "loco_compensate_quantize_ex", "loco_dequant_reduce",
-           "loco_topk_quantize", "loco_sparse_aggregate", "loco_status_string", "loco_version"]
+           "loco_dequant_reduce_adam", "loco_topk_quantize", "loco_sparse_aggregate", "loco_status_string",
+           "loco_version"]
 
 
 class LocoError(RuntimeError):
@@ -48,6 +49,11 @@ class CqOptions(ctypes.Structure):
 
 class Payload(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
+
+
+class AdamParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("delta", ctypes.c_float)]
 
 
 class SparsePayload(ctypes.Structure):
@@ -81,6 +87,11 @@ def load(path: str | None = None):
                                         ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
                                         ctypes.c_int, ctypes.c_void_p]
     lib.loco_dequant_reduce.restype = ctypes.c_int
+    lib.loco_dequant_reduce_adam.argtypes = [ctypes.POINTER(Payload), ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.POINTER(AdamParams),
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+    lib.loco_dequant_reduce_adam.restype = ctypes.c_int
     lib.loco_topk_quantize.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -198,6 +209,27 @@ def loco_dequant_reduce(peers, n: int, *, bits: int, block: int, out, out_scale:
     _check("loco_dequant_reduce", st)
 
 
+def loco_dequant_reduce_adam(peers, n: int, *, bits: int, block: int, out_scale: float, param, m, v,
+                             lr: float, beta1: float, beta2: float, delta: float, param_bf16=None,
+                             fixed_scale: float = 0.0, stream=None) -> None:
+    """peers as loco_dequant_reduce; param, m, v float32 tensors of n elements, updated in
+    place; param_bf16 an optional bfloat16 tensor that receives the new param."""
+    for t in (param, m, v):
+        if t.dtype != torch.float32:
+            raise TypeError("param, m and v must be float32")
+    if param_bf16 is not None and param_bf16.dtype != torch.bfloat16:
+        raise TypeError("param_bf16 must be bfloat16")
+    ps = list(peers)
+    arr = (Payload * max(1, len(ps)))()
+    for i, (c, a) in enumerate(ps):
+        arr[i] = Payload(_ptr(c), _ptr(a))
+    hp = AdamParams(lr, beta1, beta2, delta)
+    st = load().loco_dequant_reduce_adam(arr if ps else None, len(ps), n, bits, block, fixed_scale, out_scale,
+                                         ctypes.byref(hp), _ptr(param), _ptr(m), _ptr(v), _ptr(param_bf16),
+                                         _stream(stream))
+    _check("loco_dequant_reduce_adam", st)
+
+
 def loco_topk_quantize(grad, err, *, chunk: int, k: int, idx, codes, absmax, bits: int = 2,
                        ef_decay: float = 1.0, stream=None) -> None:
     if grad.dtype != torch.float32 or err.dtype != torch.float32:
@@ -224,5 +256,6 @@ def loco_sparse_aggregate(peers, n: int, *, chunk: int, k: int, out, out_scale: 
 compensate_quantize = loco_compensate_quantize
 compensate_quantize_ex = loco_compensate_quantize_ex
 dequant_reduce = loco_dequant_reduce
+dequant_reduce_adam = loco_dequant_reduce_adam
 topk_quantize = loco_topk_quantize
 sparse_aggregate = loco_sparse_aggregate

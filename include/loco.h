@@ -5,7 +5,8 @@
  *   "LoCo: Low-Bit Communication Adaptor for Large-scale Model Training"
  *   (arXiv 2407.04480): Sec. 3.1 Eqns. (1)-(3) compensate and compress,
  *   Sec. 3.2 Eqns. (4)-(5) the moving-average compression error,
- *   Sec. 3.3 Eqn. (8) the all2all partitions and their high-precision average.
+ *   Sec. 3.3 Eqn. (8) the all2all partitions and their high-precision average,
+ *   Sec. 4 Eqn. (9) the Adam-family step that consumes the average.
  *   "Communication Efficient LLM Pre-training with SparseLoCo" (summary and
  *   abstract): Top-k sparsification, 2-bit codes and error feedback, and the sparse
  *   aggregation of the nodes' sparse updates.
@@ -167,6 +168,37 @@ typedef struct {
 int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_t n,
                         int bits, int block, float fixed_scale, float out_scale,
                         void* out, loco_dtype_t out_dtype, void* stream);
+
+/* Hyper-parameters of the LoCo-Adam step (host struct, read during the call). */
+typedef struct {
+    float lr;     /* learning rate eta, finite */
+    float beta1;  /* weight of the new gradient in m, in [0, 1] (the page's typical 0.1) */
+    float beta2;  /* weight of the new squared gradient in v, in [0, 1] (typical 0.001-0.05) */
+    float delta;  /* finite, > 0: added to v under the square root */
+} loco_adam_t;
+
+/*
+ * loco_dequant_reduce_adam - LoCo Sec. 3.3 Eqn. (8) fused with Sec. 4 Eqn. (9): the
+ * peers' payloads are averaged exactly as loco_dequant_reduce does (fp32, peer order,
+ * times out_scale; never rounded to bf16), and the average g drives one Adam-family
+ * step on the partition's fp32 weights and moments, in one pass:
+ *   m     <- (1 - beta1) * m + beta1 * g              (1 - beta rounded to f32 first)
+ *   v     <- (1 - beta2) * v + beta2 * (g * g)
+ *   u      = 1 / sqrt(v + delta)                      (correctly rounded sqrt and divide)
+ *   param <- param - lr * (m * u)
+ * in that order of roundings, with no bias correction or weight decay (the page names
+ * neither); m and v start at 0 (the caller zeroes them).  The reduced gradient is not
+ * written anywhere.
+ *   peers, npeers, n, bits, block, fixed_scale, out_scale: as loco_dequant_reduce
+ *   adam        host pointer to the hyper-parameters
+ *   param, m, v device f32[n] each, read and updated in place
+ *   param_bf16  device u16[n] (written: the RNE bf16 copy of the new param), or NULL
+ * None of param, m, v, param_bf16 may overlap each other or a payload.
+ */
+int loco_dequant_reduce_adam(const loco_payload_t* peers, int npeers, int64_t n,
+                             int bits, int block, float fixed_scale, float out_scale,
+                             const loco_adam_t* adam, float* param, float* m, float* v,
+                             uint16_t* param_bf16, void* stream);
 
 /*
  * loco_topk_quantize - SparseLoCo-style per-chunk Top-k with low-bit codes and error

@@ -249,3 +249,32 @@ def test_sa_peer_checks(lib):
     assert sa(lib, [spl()], n=0) == OK
     # a peer's scales inside the last 16 bytes of the output
     assert sa(lib, [spl(a=A + 10000 * 4 - 16)]) == INV
+
+
+def dra(lib, peers, n=1000, bits=4, block=128, fixed=0.0, scale=0.25, hp=(1e-4, 0.1, 0.01, 1e-8), param=A,
+        m=0x7000000, v=0x7100000, pb=0, npeers=None, null_hp=False):
+    arr = (loco.Payload * max(1, len(peers)))(*peers) if peers else None
+    h = loco.AdamParams(*hp)
+    return lib.loco_dequant_reduce_adam(arr, len(peers) if npeers is None else npeers, n, bits, block, fixed, scale,
+                                        None if null_hp else ctypes.byref(h), param, m, v, pb or None, None)
+
+
+@pytest.mark.parametrize("kwargs,want", [
+    (dict(npeers=0), INV), (dict(n=-1), INV), (dict(bits=3), UNSUP), (dict(block=100), UNSUP),
+    (dict(scale=NAN), INV), (dict(null_hp=True), INV),
+    (dict(hp=(NAN, 0.1, 0.01, 1e-8)), INV), (dict(hp=(1e-4, 1.5, 0.01, 1e-8)), INV),
+    (dict(hp=(1e-4, 0.1, -0.1, 1e-8)), INV), (dict(hp=(1e-4, 0.1, 0.01, 0.0)), INV),
+    (dict(hp=(1e-4, 0.1, 0.01, math.inf)), INV),
+    (dict(param=0), INV), (dict(m=0), INV), (dict(v=0), INV),
+    (dict(param=A + 4), ALIGN), (dict(pb=0x7200000 + 2), ALIGN),
+    (dict(m=A + 16), INV),                 # m overlaps param
+    (dict(pb=0x7100000 + 64), INV),        # the bf16 copy overlaps v
+    (dict(v=Cp + 32), INV),                # v overlaps a payload's codes
+])
+def test_dra_checks(lib, kwargs, want):
+    assert dra(lib, [pl(), pl(Cp + 4096, Dp + 4096)], **kwargs) == want
+
+
+def test_dra_noop(lib):
+    assert dra(lib, [pl()], n=0) == OK
+    assert dra(lib, [pl()], n=0, param=0) == OK

@@ -186,3 +186,42 @@ def test_fullsize_sparse_aggregate(gpu_lib):
         want = oracle.sparse_aggregate(sl, C, chunk=C, k=k, bits=bits, out_scale=1.0 / P)
         assert_f32_close(host(out[c * C:(c + 1) * C]), want, np.zeros(C), f"sparse aggregate chunk {c}")
     say(f"sparse aggregate full: {len(sample)} chunks checked")
+
+
+def test_fullsize_dequant_reduce_adam_7b(gpu_lib):
+    """8 peer payloads of 105,250,000 (4-bit, block 256) averaged and fed to one Adam step on
+    fp32 weights and moments with a bf16 weight copy, as bench launches it; 2 steps on
+    sampled blocks."""
+    n, P, bits, block = W.SHARD7B_PART, W.SHARD7B_PEERS, 4, 256
+    hp = dict(lr=1e-4, beta1=0.1, beta2=0.01, delta=1e-8)
+    th = (torch.randn(n, device="cuda") * 0.02).contiguous()
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    tb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(9)
+    ranges = block_ranges(-(-n // block), rng, count=48)
+    ora = {}
+    for b0, b1 in ranges:
+        lo, hi = b0 * block, min(b1 * block, n)
+        ora[b0] = (host(th[lo:hi]).copy(), np.zeros(hi - lo, np.float32), np.zeros(hi - lo, np.float32))
+    for step in range(2):
+        say(f"dra full: step {step}, generating 8 payloads")
+        pays = [W.random_payload(n, bits, block, key=("dra-full", step, p), device="cuda") for p in range(P)]
+        gpu_lib.loco_dequant_reduce_adam(pays, n, bits=bits, block=block, out_scale=1.0 / P, param=th, m=m, v=v,
+                                         param_bf16=tb, **hp)
+        torch.cuda.synchronize()
+        for b0, b1 in ranges:
+            lo, hi = b0 * block, min(b1 * block, n)
+            sl = [(host(c[lo * bits // 8:(hi * bits + 7) // 8]), host(a[b0:b1])) for c, a in pays]
+            o_th, o_m, o_v = ora[b0]
+            ref = oracle.dequant_reduce_adam(sl, hi - lo, bits=bits, block=block, out_scale=1.0 / P, theta=o_th,
+                                             m=o_m, v=o_v, **hp)
+            z = np.zeros(hi - lo)
+            t = f"dra full step {step} blocks {b0}:{b1}"
+            assert_f32_close(host(m[lo:hi]), ref["m"], z, f"{t} m")
+            assert_f32_close(host(v[lo:hi]), ref["v"], z, f"{t} v")
+            assert_f32_close(host(th[lo:hi]), ref["theta"], z, f"{t} theta")
+            assert_bf16_close(bf16_bits(tb[lo:hi]), ref["theta_bf16"], f"{t} theta bf16")
+            ora[b0] = (ref["theta"], ref["m"], ref["v"])
+        del pays
+    say(f"dra full: {len(ranges)} block runs checked")
