@@ -13,11 +13,11 @@
 //     (12 ballot rounds, wave 0); k keys of the chunk are then >= L;
 //  2. the keys >= L (about k + a few dozen) are compacted in index order into LDS
 //     (per-wave ballot counts, a cross-wave prefix over (slot, wave) pairs, then mbcnt);
-//  3. every thread ranks its candidate against all candidates in the order (key
-//     descending, index ascending) with 16-byte broadcast LDS reads; the kept elements
-//     are exactly the candidates of rank < k, already in index order.  Their threads
-//     quantise them, write their error, index and code; the candidate of rank k-1 gives
-//     the threshold T and the last kept tie;
+//  3. wave 0 finds the threshold T (the k-th largest candidate key) by a bit search over
+//     the candidates, only over the low bits where L and the chunk's largest key differ,
+//     and the last kept tie (the candidates are in index order, so the kept ties are the
+//     first ones equal to T); the kept candidates' threads quantise them and write their
+//     error, index and code in index order;
 //  4. every other element's error is h, written by a masked store.
 // If k > 256 or more than kTkCap keys are >= L, all four waves search every key instead
 // (cross-wave counts through LDS) and every element is selected and compacted in place;
@@ -36,7 +36,7 @@ constexpr int kTkBoundLowBit = 19;
 
 struct TkShared {
     uint32_t top[kTkThreads];               // per-thread maximum key
-    alignas(16) uint32_t key[kTkCap + 4];   // candidate keys, index order, zero-padded to a 16-byte row
+    uint32_t key[kTkCap];                   // candidate keys, index order
     uint32_t hb[kTkCap];                    // candidate h bit patterns
     uint16_t idx[kTkCap];                   // candidate chunk-local indices
     int cnt[64];                            // per (slot, wave) counts, pair p = 4*slot + wave
@@ -112,9 +112,11 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
                 ev[j] = i < len ? p.e[base + i] : 0.0f;
             }
         }
+        // decay 1 skips the multiply: 1 * e is e exactly, so h is the same either way
+        const bool unit = p.decay == 1.0f;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const uint32_t u = __float_as_uint(gv[j] + p.decay * ev[j]);
+            const uint32_t u = __float_as_uint(unit ? gv[j] + ev[j] : gv[j] + p.decay * ev[j]);
             kv[j] = u & 0x7FFFFFFFu;
             sgn |= (u >> 31) << j;
         }
@@ -173,34 +175,70 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
                     sh.idx[pos] = (uint16_t)(j * kTkThreads + tid);
                 }
             }
-            if (tid < 4) sh.key[total + tid] = 0u;
             fast = true;
         }
         __syncthreads();
 
         if (fast) {
-            // D. rank every candidate; keep rank < keff
-            const int nrow = (total + 3) >> 2;
+            // D. wave 0 finds T, the keff-th largest candidate key, by a bit search over the
+            //    candidates (8 per lane at most), then the last kept tie: candidates are in
+            //    index order, so the kept ties are the first `need` candidates equal to T.
+            if (w == 0) {
+                constexpr int S = kTkCap / 64;
+                const int ns = (total + 63) >> 6;
+                uint32_t ck[S];
+#pragma unroll
+                for (int s = 0; s < S; ++s) ck[s] = (s * 64 + lane < total) ? sh.key[s * 64 + lane] : 0u;
+                // T lies in [L, M], so it keeps the high bits L and M share; search the rest
+                uint32_t T = L;
+                const uint32_t diff = L ^ M;
+                if (diff != 0u) {
+                    const int top = 31 - __builtin_clz(diff);
+                    T = L & ~((2u << top) - 1u);
+                    for (int bit = top; bit >= 0; --bit) {
+                        const uint32_t cand = T | (1u << bit);
+                        int c = 0;
+#pragma unroll
+                        for (int s = 0; s < S; ++s)
+                            if (s < ns) c += __popcll(ballot(ck[s] >= cand));
+                        if (c >= keff) T = cand;
+                    }
+                }
+                int need = keff;
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    if (s < ns) need -= __popcll(ballot(ck[s] > T));
+                int ilast = 0;
+                bool found = false;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    if (s < ns && !found) {
+                        const uint64_t b = ballot(ck[s] == T);
+                        const int pc = __popcll(b);
+                        if (need <= pc) {
+                            ilast = sh.idx[s * 64 + nth_set_bit(b, need)];
+                            found = true;
+                        } else {
+                            need -= pc;
+                        }
+                    }
+                }
+                if (lane == 0) {
+                    sh.T = T;
+                    sh.ilast = ilast;
+                }
+            }
+            __syncthreads();
+            const uint32_t T = sh.T;
+            const int ilast = sh.ilast;
             uint64_t selb[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int t = s * kTkThreads + tid;
                 bool kept = false;
-                if (s * kTkThreads + 64 * w < total) {
+                if (t < total) {
                     const uint32_t mk = sh.key[t];
-                    int rank = 0;
-                    for (int r = 0; r < nrow; ++r) {
-                        const u32x4 kr = *(const u32x4*)&sh.key[4 * r];
-                        const int c = 4 * r;
-                        rank += (kr.x > mk) + (kr.y > mk) + (kr.z > mk) + (kr.w > mk);
-                        rank += (kr.x == mk && c < t) + (kr.y == mk && c + 1 < t) + (kr.z == mk && c + 2 < t) +
-                                (kr.w == mk && c + 3 < t);
-                    }
-                    kept = t < total && rank < keff;
-                    if (t < total && rank == keff - 1) {
-                        sh.T = mk;
-                        sh.ilast = sh.idx[t];
-                    }
+                    kept = mk > T || (mk == T && (int)sh.idx[t] <= ilast);
                 }
                 selb[s] = ballot(kept);
                 if (lane == 0) sh.cnt[s * kTkWaves + w] = __popcll(selb[s]);
@@ -226,8 +264,6 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
             }
             __syncthreads();
             // E. every element that is not kept keeps its whole h as error
-            const uint32_t T = sh.T;
-            const int ilast = sh.ilast;
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int i = j * kTkThreads + tid;
