@@ -30,7 +30,7 @@ namespace loco {
 #define LOCO_DR_THREADS 256
 #endif
 #ifndef LOCO_TK_WAVES_PER_EU
-#define LOCO_TK_WAVES_PER_EU 4
+#define LOCO_TK_WAVES_PER_EU 5
 #endif
 #ifndef LOCO_CQ_XCD_RUN
 #define LOCO_CQ_XCD_RUN 32

@@ -2,26 +2,29 @@
 // error feedback ("Communication Efficient LLM Pre-training with SparseLoCo": Top-k
 // sparsification, 2-bit quantisation, error feedback).
 //
-// One 256-thread workgroup (4 waves) owns one chunk of C = 256*VPT elements; element
-// i = 256*j + 64*w + lane sits in slot j of lane `lane` of wave w, so every global access
-// is a 256-byte coalesced row per wave and (slot, wave, lane) order is index order.
-// Each element is held as its key bits(|h|) plus one sign bit, VPT keys per lane.
+// One 256-thread workgroup (4 waves) owns one chunk of C = 256*VPT elements.  Thread t
+// holds Q = VPT/R groups of R consecutive elements (R = min(4, VPT)): element
+// i = q*256*R + t*R + r, so each load and store instruction of a wave covers one
+// contiguous row of 64*R elements, and index order is (q, t, r) order.  h = g + decay*e
+// is also kept in LDS, where the kept elements receive their new error before the whole
+// chunk's error is copied out.
 //
-// Exact selection of the k kept elements (largest keys, ties to the lower index):
+// Exact selection of the k kept elements (largest |h|, compared as the bit pattern
+// ("key"); ties to the lower index):
 //  1. a lower bound L of the k-th largest key: the largest value with 12 significant key
 //     bits (exponent and 4 mantissa bits) that at least k per-thread maxima reach
 //     (12 ballot rounds, wave 0); k keys of the chunk are then >= L;
-//  2. the keys >= L (about k + a few dozen) are compacted in index order into LDS
-//     (per-wave ballot counts, a cross-wave prefix over (slot, wave) pairs, then mbcnt);
+//  2. the keys >= L (about k + a few dozen) are compacted in index order into LDS (a
+//     workgroup prefix over the per-(q, thread) counts);
 //  3. wave 0 finds the threshold T (the k-th largest candidate key) by a bit search over
 //     the candidates, only over the low bits where L and the chunk's largest key differ,
 //     and the last kept tie (the candidates are in index order, so the kept ties are the
-//     first ones equal to T); the kept candidates' threads quantise them and write their
-//     error, index and code in index order;
-//  4. every other element's error is h, written by a masked store.
+//     first ones equal to T); the kept candidates' threads quantise them, write their new
+//     error into the LDS copy of h, and their index and code in index order;
+//  4. the LDS copy (h, or the new error where kept) is the chunk's new error.
 // If k > 256 or more than kTkCap keys are >= L, all four waves search every key instead
-// (cross-wave counts through LDS) and every element is selected and compacted in place;
-// the result is the same exact set.
+// (cross-wave counts through LDS), and the kept elements are compacted over the whole
+// chunk; the result is the same exact set.
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"
@@ -34,17 +37,19 @@ constexpr int kTkWaves = kTkThreads / kWave;
 // The lower bound L keeps key bits 30..kTkBoundLowBit (exponent + 4 mantissa bits).
 constexpr int kTkBoundLowBit = 19;
 
+template <int C>
 struct TkShared {
-    uint32_t top[kTkThreads];               // per-thread maximum key
-    uint32_t key[kTkCap];                   // candidate keys, index order
-    uint32_t hb[kTkCap];                    // candidate h bit patterns
-    uint16_t idx[kTkCap];                   // candidate chunk-local indices
-    int cnt[64];                            // per (slot, wave) counts, pair p = 4*slot + wave
-    uint32_t wmax[kTkWaves];
+    uint32_t h[C];                  // h bits; kept elements get their new error
+    uint32_t top[kTkThreads];       // per-thread maximum key
+    uint32_t key[kTkCap];           // candidate keys, index order
+    uint16_t idx[kTkCap];           // candidate chunk-local indices
+    uint8_t code[C];                // kept codes, index order (k <= C)
+    int wsum[2][kTkWaves][2];       // per-wave totals of the packed prefix scans (two buffers)
+    int cnt[2 * kTkWaves];          // kept candidates per (candidate slot, wave)
     int red[kTkWaves];
+    uint32_t wmax[kTkWaves];
     uint32_t L, T;
     int ilast;
-    uint8_t code[4096];                     // kept codes, index order (k <= C <= 4096)
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -57,13 +62,44 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Exclusive prefix of sh.cnt[0..NP) held by lane p for pair p; `total` is the sum.
-template <int NP>
-__device__ __forceinline__ int pair_prefix(const TkShared& sh, int lane, int& total) {
-    const int v = lane < NP ? sh.cnt[lane] : 0;
-    const int incl = wave_incl_scan(v, lane);
-    total = __builtin_amdgcn_readlane(incl, 63);
-    return incl - v;
+// Exclusive prefix over the workgroup's threads (thread order) of per-thread counts of up
+// to 4 groups, each below 2^16 in total: groups 0 and 1 are packed into one int (bits
+// 0-15, 16-31), groups 2 and 3 into another, and each packed int is scanned once.
+// Returns each group's exclusive prefix in pre[q] and its total over all threads in
+// tot[q].  `buf` picks one of two LDS buffers, so two calls separated by a barrier do not
+// collide.  Contains one barrier.
+template <int Q, class SH>
+__device__ __forceinline__ void block_scan(const int (&cnt)[4], int lane, int w, SH& sh, int buf,
+                                           int (&pre)[4], int (&tot)[4]) {
+    const int a = cnt[0] | (Q > 1 ? cnt[1] << 16 : 0);
+    const int b = (Q > 2 ? cnt[2] : 0) | (Q > 3 ? cnt[3] << 16 : 0);
+    const int ia = wave_incl_scan(a, lane);
+    const int ib = Q > 2 ? wave_incl_scan(b, lane) : 0;
+    if (lane == 63) {
+        sh.wsum[buf][w][0] = ia;
+        sh.wsum[buf][w][1] = ib;
+    }
+    __syncthreads();
+    int ba = 0, bb = 0, ta = 0, tb = 0;
+#pragma unroll
+    for (int x = 0; x < kTkWaves; ++x) {
+        const int sa = sh.wsum[buf][x][0], sb = sh.wsum[buf][x][1];
+        ta += sa;
+        tb += sb;
+        if (x < w) {
+            ba += sa;
+            bb += sb;
+        }
+    }
+    const int ea = ba + ia - a, eb = bb + ib - b;  // exclusive, still packed
+    pre[0] = ea & 0xFFFF;
+    pre[1] = (ea >> 16) & 0xFFFF;
+    pre[2] = eb & 0xFFFF;
+    pre[3] = (eb >> 16) & 0xFFFF;
+    tot[0] = ta & 0xFFFF;
+    tot[1] = (ta >> 16) & 0xFFFF;
+    tot[2] = tb & 0xFFFF;
+    tot[3] = (tb >> 16) & 0xFFFF;
 }
 
 template <int BITS>
@@ -72,17 +108,30 @@ __device__ __forceinline__ int quantise(float h, float inv) {
     return (int)__builtin_amdgcn_fmed3f(__builtin_rintf(h * inv), (float)(-QMAX - 1), (float)QMAX);
 }
 
-__device__ __forceinline__ float h_of(uint32_t key, uint32_t sgn, int j) {
-    return __uint_as_float(key | ((sgn >> j) & 1u) << 31);
+// R consecutive floats at p (R in {1, 2, 4}; p aligned to 4*R bytes).
+template <int R, bool NT>
+__device__ __forceinline__ void loadr(const float* p, float* x) {
+    if constexpr (R == 4) {
+        const f32x4 v = NT ? __builtin_nontemporal_load((const f32x4*)p) : *(const f32x4*)p;
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    } else if constexpr (R == 2) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 v = NT ? __builtin_nontemporal_load((const f32x2*)p) : *(const f32x2*)p;
+        x[0] = v.x; x[1] = v.y;
+    } else {
+        x[0] = NT ? __builtin_nontemporal_load(p) : *p;
+    }
 }
 
-// FULL: the chunk has all C elements (every chunk but a short last one); the loads and
-// stores of a full chunk are straight-line code, so all of them are in flight at once.
+// FULL: the chunk has all C elements (every chunk but a short last one); its loads and
+// stores are whole vectors with no bounds masks.
 template <int VPT, int BITS, bool FULL>
-__device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkShared& sh) {
+__device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkShared<kTkThreads * VPT>& sh) {
     static_assert(VPT <= 16, "C <= 4096");
     constexpr int C = kTkThreads * VPT;
-    constexpr int NP = kTkWaves * VPT;
+    constexpr int R = VPT < 4 ? VPT : 4;
+    constexpr int Q = VPT / R;
+    constexpr int ROW = kTkThreads * R;  // elements per group row
     constexpr int QMAX = (1 << (BITS - 1)) - 1;
     constexpr uint32_t CMASK = (1u << BITS) - 1u;
     const int tid = threadIdx.x;
@@ -94,36 +143,49 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
     const int keff = p.k < len ? p.k : len;
     uint16_t* idx_out = p.idx + chunk * p.k;
 
-    // A. h = g + decay * e as key + sign; elements past the end of a short chunk get key 0,
-    //    which no threshold tried below (>= 1) admits and which loses every tie to a real
-    //    element of lower index (keff <= len).
-    uint32_t kv[VPT];
-    uint32_t sgn = 0;
+    // A. h = g + decay * e; its key goes to registers, h itself to LDS.  Elements past the
+    //    end of a short chunk get key 0, which no threshold tried below (>= 1) admits and
+    //    which loses every tie to a real element of lower index (keff <= len).
+    uint32_t kv[Q][R];
     {
-        float gv[VPT], ev[VPT];
+        float gv[Q][R], ev[Q][R];
+        const float* gb = p.g + base;
+        const float* eb = p.e + base;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int i = j * kTkThreads + tid;
+        for (int q = 0; q < Q; ++q) {
+            const int i0 = q * ROW + tid * R;
             if (FULL) {
-                gv[j] = __builtin_nontemporal_load(p.g + base + i);
-                ev[j] = p.e[base + i];
+                loadr<R, true>(gb + i0, gv[q]);
+                loadr<R, false>(eb + i0, ev[q]);
             } else {
-                gv[j] = i < len ? p.g[base + i] : 0.0f;
-                ev[j] = i < len ? p.e[base + i] : 0.0f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    gv[q][r] = i0 + r < len ? gb[i0 + r] : 0.0f;
+                    ev[q][r] = i0 + r < len ? eb[i0 + r] : 0.0f;
+                }
             }
         }
         // decay 1 skips the multiply: 1 * e is e exactly, so h is the same either way
         const bool unit = p.decay == 1.0f;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const uint32_t u = __float_as_uint(unit ? gv[j] + ev[j] : gv[j] + p.decay * ev[j]);
-            kv[j] = u & 0x7FFFFFFFu;
-            sgn |= (u >> 31) << j;
+        for (int q = 0; q < Q; ++q) {
+            uint32_t hb[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                hb[r] = __float_as_uint(unit ? gv[q][r] + ev[q][r] : gv[q][r] + p.decay * ev[q][r]);
+                kv[q][r] = hb[r] & 0x7FFFFFFFu;
+            }
+            uint32_t* hs = &sh.h[q * ROW + tid * R];
+            if constexpr (R == 4) *(u32x4*)hs = u32x4{hb[0], hb[1], hb[2], hb[3]};
+            else if constexpr (R == 2) *(u32x2*)hs = u32x2{hb[0], hb[1]};
+            else hs[0] = hb[0];
         }
     }
     uint32_t m1 = 0;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) m1 = max(m1, kv[j]);
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r) m1 = max(m1, kv[q][r]);
     const uint32_t wm = wave_max_u32(m1);
     if (lane == 0) sh.wmax[w] = wm;
     sh.top[tid] = m1;
@@ -153,27 +215,30 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
 
         // C. compact the keys >= L in index order
         const uint32_t L = sh.L;
+        int cnt[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int c = __popcll(ballot(kv[j] >= L));
-            if (lane == 0) sh.cnt[j * kTkWaves + w] = c;
-        }
-        __syncthreads();
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int r = 0; r < R; ++r) cnt[q] += kv[q][r] >= L ? 1 : 0;
+        int pre[4], tot[4];
+        block_scan<Q>(cnt, lane, w, sh, 0, pre, tot);
         int total = 0;
-        const int excl = pair_prefix<NP>(sh, lane, total);
-        if (total <= kTkCap) {
 #pragma unroll
-            for (int j = 0; j < VPT; ++j) {
-                // read the pair's base in uniform control flow: a lane read inside the
-                // divergent branch below could be an inactive one
-                const int bj = __builtin_amdgcn_readlane(excl, j * kTkWaves + w);
-                const uint64_t b = ballot(kv[j] >= L);  // taken again rather than kept: SGPRs are short
-                if (kv[j] >= L) {
-                    const int pos = bj + mbcnt(b);
-                    sh.key[pos] = kv[j];
-                    sh.hb[pos] = kv[j] | ((sgn >> j) & 1u) << 31;
-                    sh.idx[pos] = (uint16_t)(j * kTkThreads + tid);
+        for (int q = 0; q < Q; ++q) total += tot[q];
+        if (total <= kTkCap) {
+            int gbase = 0;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                int pos = gbase + pre[q];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (kv[q][r] >= L) {
+                        sh.key[pos] = kv[q][r];
+                        sh.idx[pos] = (uint16_t)(q * ROW + tid * R + r);
+                        ++pos;
+                    }
                 }
+                gbase += tot[q];
             }
             fast = true;
         }
@@ -244,31 +309,25 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
                 if (lane == 0) sh.cnt[s * kTkWaves + w] = __popcll(selb[s]);
             }
             __syncthreads();
-            int nkept = 0;
-            const int kex = pair_prefix<2 * kTkWaves>(sh, lane, nkept);
+            // the kept candidates, in index order: quantise, new error into the LDS copy,
+            // index and code
+            const int v = lane < 2 * kTkWaves ? sh.cnt[lane] : 0;
+            const int kex = wave_incl_scan(v, lane) - v;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int bs = __builtin_amdgcn_readlane(kex, s * kTkWaves + w);  // uniform control flow
                 if ((selb[s] >> lane) & 1u) {
                     const int t = s * kTkThreads + tid;
                     const int pos = bs + mbcnt(selb[s]);
-                    const float h = __uint_as_float(sh.hb[t]);
                     const int i = sh.idx[t];
+                    const float h = __uint_as_float(sh.h[i]);
                     const int q = quantise<BITS>(h, inv);
-                    p.e[base + i] = h - (float)q * step;
+                    sh.h[i] = __float_as_uint(h - (float)q * step);
                     if (pos < keff) {
                         idx_out[pos] = (uint16_t)i;
                         sh.code[pos] = (uint8_t)((uint32_t)q & CMASK);
                     }
                 }
-            }
-            __syncthreads();
-            // E. every element that is not kept keeps its whole h as error
-#pragma unroll
-            for (int j = 0; j < VPT; ++j) {
-                const int i = j * kTkThreads + tid;
-                const bool kept = kv[j] > T || (kv[j] == T && i <= ilast);
-                if (!kept && (FULL || i < len)) p.e[base + i] = h_of(kv[j], sgn, j);
             }
         }
     }
@@ -280,76 +339,104 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
             const uint32_t cand = T | (1u << bit);
             int c = 0;
 #pragma unroll
-            for (int j = 0; j < VPT; ++j) c += __popcll(ballot(kv[j] >= cand));
+            for (int q = 0; q < Q; ++q)
+#pragma unroll
+                for (int r = 0; r < R; ++r) c += __popcll(ballot(kv[q][r] >= cand));
             if (lane == 0) sh.red[w] = c;
             __syncthreads();
             c = sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3];
             __syncthreads();
             if (c >= keff) T = cand;
         }
+        // ties: the kept ones are the first `need` keys equal to T in index order
         int gt = 0;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) gt += __popcll(ballot(kv[j] > T));
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int r = 0; r < R; ++r) gt += __popcll(ballot(kv[q][r] > T));
         if (lane == 0) sh.red[w] = gt;
+        int teq[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int c = __popcll(ballot(kv[j] == T));
-            if (lane == 0) sh.cnt[j * kTkWaves + w] = c;
-        }
-        __syncthreads();
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int r = 0; r < R; ++r) teq[q] += kv[q][r] == T ? 1 : 0;
+        int tpre[4], ttot[4];
+        block_scan<Q>(teq, lane, w, sh, 1, tpre, ttot);  // its barrier also publishes sh.red
         const int need = keff - (sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3]);
-        int ties = 0;
-        const int excl = pair_prefix<NP>(sh, lane, ties);
-        // the first (slot, wave) pair whose running tie count reaches `need` holds the last
-        // kept tie
-        const int mine = lane < NP ? sh.cnt[lane] : 0;
-        const uint64_t reach = ballot(lane < NP && excl + mine >= need);
-        const int pstar = reach ? __builtin_ctzll(reach) : 0;
-        const int before = __builtin_amdgcn_readlane(excl, pstar);
-        __syncthreads();
+        // the thread whose tie range holds the need-th tie records its index
+        {
+            int gbase = 0;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const uint64_t b = ballot(kv[j] == T);  // uniform control flow
-            if (j == pstar / kTkWaves && w == pstar % kTkWaves && lane == 0)
-                sh.ilast = j * kTkThreads + w * 64 + nth_set_bit(b, need - before);
+            for (int q = 0; q < Q; ++q) {
+                int seen = gbase + tpre[q];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (kv[q][r] == T) {
+                        ++seen;
+                        if (seen == need) sh.ilast = q * ROW + tid * R + r;
+                    }
+                }
+                gbase += ttot[q];
+            }
         }
         __syncthreads();
         const int ilast = sh.ilast;
 
-        // E'. count the kept elements per (slot, wave), then write every element's error
-        //     and compact the kept ones (their ballots are taken again, in uniform flow)
+        // E'. compact the kept elements over the whole chunk: new error into the LDS copy,
+        //     index and code in index order
+        int kc[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const bool kept = kv[j] > T || (kv[j] == T && j * kTkThreads + tid <= ilast);
-            const int c = __popcll(ballot(kept));
-            if (lane == 0) sh.cnt[j * kTkWaves + w] = c;
-        }
-        __syncthreads();
-        int nkept = 0;
-        const int kex = pair_prefix<NP>(sh, lane, nkept);
+        for (int q = 0; q < Q; ++q)
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int i = j * kTkThreads + tid;
-            const bool kept = kv[j] > T || (kv[j] == T && i <= ilast);
-            const uint64_t b = ballot(kept);
-            const int bj = __builtin_amdgcn_readlane(kex, j * kTkWaves + w);  // uniform control flow
-            const float h = h_of(kv[j], sgn, j);
-            if (kept) {
-                // pos < keff when the selection is right; the guard keeps a wrong selection
-                // from writing outside this chunk's slots
-                const int pos = bj + mbcnt(b);
-                const int q = quantise<BITS>(h, inv);
-                p.e[base + i] = h - (float)q * step;
-                if (pos < keff) {
-                    idx_out[pos] = (uint16_t)i;
-                    sh.code[pos] = (uint8_t)((uint32_t)q & CMASK);
-                }
-            } else if (FULL || i < len) {
-                p.e[base + i] = h;
+            for (int r = 0; r < R; ++r) {
+                const int i = q * ROW + tid * R + r;
+                kc[q] += (kv[q][r] > T || (kv[q][r] == T && i <= ilast)) ? 1 : 0;
             }
+        int kpre[4], ktot[4];
+        block_scan<Q>(kc, lane, w, sh, 0, kpre, ktot);
+        int gbase = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            int pos = gbase + kpre[q];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int i = q * ROW + tid * R + r;
+                if (kv[q][r] > T || (kv[q][r] == T && i <= ilast)) {
+                    const float h = __uint_as_float(sh.h[i]);
+                    const int qc = quantise<BITS>(h, inv);
+                    sh.h[i] = __float_as_uint(h - (float)qc * step);
+                    // pos < keff when the selection is right; the guard keeps a wrong
+                    // selection from writing outside this chunk's slots
+                    if (pos < keff) {
+                        idx_out[pos] = (uint16_t)i;
+                        sh.code[pos] = (uint8_t)((uint32_t)qc & CMASK);
+                    }
+                    ++pos;
+                }
+            }
+            gbase += ktot[q];
         }
     }
     __syncthreads();
+
+    // E. the chunk's new error: h, or the kept elements' residual, copied out of LDS
+    {
+        float* eb = p.e + base;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int i0 = q * ROW + tid * R;
+            const uint32_t* hs = &sh.h[i0];
+            if (FULL) {
+                if constexpr (R == 4) *(u32x4*)(eb + i0) = *(const u32x4*)hs;
+                else if constexpr (R == 2) *(u32x2*)(eb + i0) = *(const u32x2*)hs;
+                else *(uint32_t*)(eb + i0) = hs[0];
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (i0 + r < len) eb[i0 + r] = __uint_as_float(hs[r]);
+            }
+        }
+    }
 
     // F. unused slots, packed codes, scale
     for (int pos = keff + tid; pos < p.k; pos += kTkThreads) idx_out[pos] = 0xFFFF;
@@ -374,7 +461,7 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
 template <int VPT, int BITS, bool FULL>
 __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(LOCO_TK_WAVES_PER_EU)))
 void tk_kernel(TkParams p, int64_t c0, int64_t c1) {
-    __shared__ TkShared sh;
+    __shared__ TkShared<kTkThreads * VPT> sh;
     for (int64_t c = c0 + blockIdx.x; c < c1; c += gridDim.x) {
         tk_chunk<VPT, BITS, FULL>(p, c, sh);
         __syncthreads();
