@@ -114,10 +114,20 @@ def cpu_baseline(g_dev, payloads_dev, slab, min_seconds=10.0):
         spent += time.perf_counter() - t0
         done += slab
     per_step = spent / steps
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"value": round(done * 2 / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done:,} of the shard's {n:,} elements in slabs of {slab:,} (one segment each) + the "
                       f"matching 1/8 of each of the 8 peer payloads, 2 steps per slab, {spent:.1f} s of oracle "
-                      f"time; NumPy element-wise, one thread (host shows {os.cpu_count()} cores)"}
+                      f"time; NumPy element-wise, one thread ({avail} cores available to the process, {model})"}
 
 
 def main():
@@ -236,9 +246,9 @@ def main():
         segs8 = [(g[i * part:(i + 1) * part], e8[i * part:(i + 1) * part], codes8[i], absmax[i])
                  for i in range(PARTS)]
         ms = timed(lambda: loco.loco_compensate_quantize(segs8, bits=8, block=BLOCK, beta=BETA, stream=stream),
-                   stream, max(3, args.steps // 3))
+                   stream, max(10, args.steps // 2))
         b8 = cq_bytes(sizes, 2, 4, 8, BLOCK)
-        modes["compensate_quantize_8bit_7b_shard"] = {"avg_ms": round(ms, 4), "alg_bytes": b8,
+        modes["compensate_quantize_8bit_7b_shard"] = {"avg_ms": round(ms, 4), **spread(), "alg_bytes": b8,
                                                       "GBps": round(b8 / ms / 1e6, 1),
                                                       "frac_hbm": round(b8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                                       "grad_GBps": round(n * 2 / ms / 1e6, 1)}
@@ -248,9 +258,9 @@ def main():
         segs_i8 = [(g[i * part:(i + 1) * part], ei8[i * part:(i + 1) * part], *segs[i][2:]) for i in range(PARTS)]
         ms = timed(lambda: loco.loco_compensate_quantize_ex(segs_i8, bits=BITS, block=BLOCK, beta=BETA,
                                                             err_scale=2.0 ** 17, stream=stream),
-                   stream, max(3, args.steps // 3))
+                   stream, max(10, args.steps // 2))
         bi8 = cq_bytes(sizes, 2, 1, BITS, BLOCK)
-        modes["compensate_quantize_4bit_i8err_7b_shard"] = {"avg_ms": round(ms, 4), "alg_bytes": bi8,
+        modes["compensate_quantize_4bit_i8err_7b_shard"] = {"avg_ms": round(ms, 4), **spread(), "alg_bytes": bi8,
                                                             "GBps": round(bi8 / ms / 1e6, 1),
                                                             "frac_hbm": round(bi8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                                             "grad_GBps": round(n * 2 / ms / 1e6, 1),
@@ -265,11 +275,11 @@ def main():
         ms = timed(lambda: loco.loco_dequant_reduce_adam(payloads, part, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS,
                                                          param=th, m=m_, v=v_, lr=1e-4, beta1=0.1, beta2=0.01,
                                                          delta=1e-8, param_bf16=tb, stream=stream),
-                   stream, max(3, args.steps // 3))
+                   stream, max(10, args.steps // 2))
         bda = dr_bytes(part, PARTS, BITS, BLOCK, 0) + 26 * part
         modes["dequant_reduce_adam_8peers"] = {"workload": f"8 peer 4-bit payloads of {part:,} averaged into one "
                                                            "Adam step (fp32 weights, m, v; bf16 weight copy)",
-                                               "avg_ms": round(ms, 4), "alg_bytes": bda,
+                                               "avg_ms": round(ms, 4), **spread(), "alg_bytes": bda,
                                                "GBps": round(bda / ms / 1e6, 1),
                                                "frac_hbm": round(bda / ms / 1e6 / HBM_PEAK_GBPS, 4)}
         del th, m_, v_, tb
@@ -283,11 +293,11 @@ def main():
         tabs = torch.empty(chunks, dtype=torch.float32, device=dev)
         ms = timed(lambda: loco.loco_topk_quantize(gt, et, chunk=TK_CHUNK, k=TK_K, idx=idx, codes=tcodes,
                                                    absmax=tabs, bits=2, ef_decay=1.0, stream=stream),
-                   stream, max(3, args.steps // 3))
+                   stream, max(10, args.steps // 2))
         bt = tk_bytes(nt, TK_CHUNK, TK_K, 2)
         modes["sparseloco_topk_2bit"] = {"workload": f"{nt:,} fp32 N(0,1e-3) + 0.1% +-0.1 outliers, chunk 4096, "
                                                      f"k=82, 2-bit, fp32 error feedback",
-                                         "avg_ms": round(ms, 4), "alg_bytes": bt, "GBps": round(bt / ms / 1e6, 1),
+                                         "avg_ms": round(ms, 4), **spread(), "alg_bytes": bt, "GBps": round(bt / ms / 1e6, 1),
                                          "frac_hbm": round(bt / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                          "grad_GBps": round(nt * 4 / ms / 1e6, 1)}
         del gt, et, idx, tcodes, tabs
@@ -296,11 +306,11 @@ def main():
         sout = torch.empty(nt, dtype=torch.float32, device=dev)
         ms = timed(lambda: loco.loco_sparse_aggregate(spays, nt, chunk=TK_CHUNK, k=TK_K, bits=2, out=sout,
                                                       out_scale=1.0 / PARTS, stream=stream),
-                   stream, max(3, args.steps // 3))
+                   stream, max(10, args.steps // 2))
         bs = sa_bytes(nt, PARTS, TK_CHUNK, TK_K, 2, 4)
         modes["sparseloco_aggregate_8peers"] = {"workload": f"8 peers' Top-k payloads of {nt:,} (chunk 4096, k=82, "
                                                             f"2-bit) into fp32 x 1/8",
-                                                "avg_ms": round(ms, 4), "alg_bytes": bs,
+                                                "avg_ms": round(ms, 4), **spread(), "alg_bytes": bs,
                                                 "GBps": round(bs / ms / 1e6, 1),
                                                 "frac_hbm": round(bs / ms / 1e6 / HBM_PEAK_GBPS, 4)}
         del spays, sout
@@ -332,18 +342,39 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+_FLUSH = None
+
+
 def timed(fn, stream, reps):
+    """Average launch time in ms (HIP events on `stream`) over `reps` launches after 2
+    warm-ups.  Before each launch a 1 GiB buffer is written (outside the timed pair), so no
+    launch finds the previous one's data in the 256 MB Infinity Cache.  The sorted
+    per-launch times are kept in timed.last."""
     import torch
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
+    with torch.cuda.stream(stream):
+        for i, (a, b) in enumerate(evs):
+            _FLUSH.fill_(float(i))
+            a.record(stream)
+            fn()
+            b.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / reps
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    timed.last = ms
+    return sum(ms) / reps
+
+
+def spread():
+    """Median, p10 and p90 (ms) of the last timed() call."""
+    ms = timed.last
+    return {"median_ms": round(ms[len(ms) // 2], 4), "p10_ms": round(ms[len(ms) // 10], 4),
+            "p90_ms": round(ms[(len(ms) * 9) // 10], 4)}
 
 
 if __name__ == "__main__":

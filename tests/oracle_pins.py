@@ -420,6 +420,78 @@ def pin_i8_compressor_vs_torch(O):
         assert np.array_equal(O.error_decompress(want, s_e), want.astype(F32) / F32(s_e))
 
 
+# -- scalar twins: the same steps element by element, in fp32 scalars, on tiny inputs ------------
+
+def _decode(codes, j, bits):
+    """Code j of a packed array by the layout rule (little end first, two's complement)."""
+    bit = j * bits
+    raw = (int(codes[bit // 8]) >> (bit % 8)) & ((1 << bits) - 1)
+    return raw - (1 << bits) if raw >= (1 << (bits - 1)) else raw
+
+
+def _cq_twin(g, e, bits, block, beta):
+    qmax = (1 << (bits - 1)) - 1
+    n = len(g)
+    b, om = F32(beta), F32(1) - F32(beta)
+    h = [F32(F32(g[i]) + F32(e[i])) for i in range(n)]
+    q, absmax, e_new = [0] * n, [], [F32(0)] * n
+    for b0 in range(0, n, block):
+        idx = range(b0, min(n, b0 + block))
+        am = F32(0)
+        for i in idx:
+            am = max(am, F32(abs(h[i])))
+        step = F32(am / F32(qmax)) if am != 0 else F32(0)
+        inv = F32(F32(1) / step) if am != 0 else F32(0)
+        absmax.append(am)
+        for i in idx:
+            q[i] = int(min(max(np.rint(F32(h[i] * inv)), -qmax - 1), qmax))
+            d = F32(F32(q[i]) * step)
+            r = F32(h[i] - d)
+            e_new[i] = F32(F32(b * F32(e[i])) + F32(om * r))
+    packed = [0] * (-(-n * bits // 8))
+    for i, c in enumerate(q):
+        packed[i * bits // 8] |= (c & ((1 << bits) - 1)) << (i * bits % 8)
+    return bytes(packed), np.array(absmax, F32), np.array(e_new, F32)
+
+
+def pin_cq_scalar_twin(O):
+    """compensate_quantize against an element-by-element fp32 scalar twin that packs by the
+    layout rule: bit-exact codes, absmax and error, for every code width, ragged blocks."""
+    rng = _rng(50)
+    for bits in (2, 4, 8):
+        for n, block, beta in ((37, 8, 0.9), (64, 16, 0.5), (13, 4, 0.0), (29, 64, 1.0)):
+            g = (rng.standard_normal(n) * 1e-3).astype(F32)
+            e = (rng.standard_normal(n) * 1e-4).astype(F32)
+            g[rng.random(n) < 0.1] = 0
+            codes, am, en = _cq_twin(g, e, bits, block, beta)
+            out = O.compensate_quantize(g, e, bits=bits, block=block, beta=beta)
+            assert out["codes"].tobytes() == codes, (bits, n, block)
+            assert np.array_equal(out["absmax"].view(np.uint32), am.view(np.uint32))
+            assert np.array_equal(out["e_new"].view(np.uint32), en.view(np.uint32)), (bits, n, block, beta)
+
+
+def pin_dr_scalar_twin(O):
+    """dequant_reduce against an element-by-element fp32 scalar twin decoding the bytes by
+    the layout rule, peers added in order."""
+    rng = _rng(51)
+    for bits in (2, 4, 8):
+        qmax = (1 << (bits - 1)) - 1
+        n, block, npeers, scale = 45, 8, 3, 1.0 / 3.0
+        peers = [(rng.integers(0, 256, -(-n * bits // 8)).astype(np.uint8),
+                  (rng.random(-(-n // block)) * 1e-2).astype(F32)) for _ in range(npeers)]
+        peers[1][1][2] = 0
+        want = []
+        for i in range(n):
+            acc = F32(0)
+            for codes, am in peers:
+                a = F32(am[i // block])
+                step = F32(a / F32(qmax)) if a != 0 else F32(0)
+                acc = F32(acc + F32(F32(_decode(codes, i, bits)) * step))
+            want.append(F32(acc * F32(scale)))
+        got = O.dequant_reduce(peers, n, bits=bits, block=block, out_scale=scale)
+        assert np.array_equal(got.view(np.uint32), np.array(want, F32).view(np.uint32)), bits
+
+
 # -- SparseLoCo sparse aggregation (SparseLoCo summary; LoCo Sec. 3.3, Eqn. (8)) -----------------
 
 def pin_sa_worked(O):
@@ -593,5 +665,5 @@ ALL_PINS = [
     pin_dequant_reduce, pin_zero_blocks, pin_bf16_rne, pin_topk_error_feedback,
     pin_i8_error_accounting, pin_i8_equals_float_when_exact, pin_reset, pin_i8_compressor_vs_torch,
     pin_sa_worked, pin_sa_brute_force, pin_sa_dense_equivalent, pin_sa_transmits_topk,
-    pin_adam_worked, pin_adam_closed_form, pin_adam_limits,
+    pin_adam_worked, pin_adam_closed_form, pin_adam_limits, pin_cq_scalar_twin, pin_dr_scalar_twin,
 ]
