@@ -347,20 +347,21 @@ _FLUSH = None
 
 def timed(fn, stream, reps):
     """Average launch time in ms (HIP events on `stream`) over `reps` launches after 2
-    warm-ups.  Before each launch a 1 GiB buffer is written (outside the timed pair), so no
-    launch finds the previous one's data in the 256 MB Infinity Cache.  The sorted
-    per-launch times are kept in timed.last."""
+    warm-ups.  Before each launch a 1 GiB buffer is read (outside the timed pair), so no
+    launch finds the previous one's data in the 256 MB Infinity Cache, and no dirty lines
+    of the flush are left for the launch to write back.  The sorted per-launch times are
+    kept in timed.last."""
     import torch
     global _FLUSH
     if _FLUSH is None:
-        _FLUSH = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        _FLUSH = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     with torch.cuda.stream(stream):
-        for i, (a, b) in enumerate(evs):
-            _FLUSH.fill_(float(i))
+        for a, b in evs:
+            _FLUSH.sum()
             a.record(stream)
             fn()
             b.record(stream)

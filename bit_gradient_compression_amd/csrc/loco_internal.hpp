@@ -36,7 +36,7 @@ namespace loco {
 #define LOCO_CQ_XCD_RUN 32
 #endif
 #ifndef LOCO_SA_XCD_RUN
-#define LOCO_SA_XCD_RUN 16
+#define LOCO_SA_XCD_RUN 64
 #endif
 #ifndef LOCO_DR_XCD_RUN
 #define LOCO_DR_XCD_RUN 16
@@ -153,15 +153,29 @@ hipError_t launch_tk(const TkParams& p, int chunk, int bits, hipStream_t stream)
 
 // ---- sparse aggregation ------------------------------------------------------------
 
+#ifndef LOCO_SA_WG_PER_CU_F32
+#define LOCO_SA_WG_PER_CU_F32 6
+#endif
+#ifndef LOCO_SA_WG_PER_CU_BF16
+#define LOCO_SA_WG_PER_CU_BF16 8
+#endif
+#ifndef LOCO_SA_VEC_F32
+#define LOCO_SA_VEC_F32 4
+#endif
 #ifndef LOCO_SA_THREADS_F32
-#define LOCO_SA_THREADS_F32 256
+#define LOCO_SA_THREADS_F32 128
 #endif
 #ifndef LOCO_SA_THREADS_BF16
 #define LOCO_SA_THREADS_BF16 128
 #endif
 constexpr int kSaThreadsF32 = LOCO_SA_THREADS_F32;    // threads per chunk, fp32 output
 constexpr int kSaThreadsBf16 = LOCO_SA_THREADS_BF16;  // threads per chunk, bf16 output
-constexpr int kSaPeerBatch = 8;    // peers whose first slot is loaded together
+constexpr int kSaPeerBatch = 8;  // peers whose first slot is loaded together
+// Workgroups per compute unit of the persistent grid, per output type: each workgroup
+// takes every gridDim.x-th chunk and loads the next chunk's payload while it processes
+// the current one (0: one workgroup per chunk, no prefetch).
+constexpr int kSaWgPerCuF32 = LOCO_SA_WG_PER_CU_F32;
+constexpr int kSaWgPerCuBf16 = LOCO_SA_WG_PER_CU_BF16;
 
 struct SaPeerDev {
     const uint16_t* idx;
