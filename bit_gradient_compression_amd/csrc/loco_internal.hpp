@@ -151,6 +151,24 @@ struct TkParams {
 
 hipError_t launch_tk(const TkParams& p, int chunk, int bits, hipStream_t stream);
 
+// Compute units of the current device, queried once per device and kept (so launches that
+// size a persistent grid make no device query while a caller captures a graph).
+inline hipError_t compute_units(int& cus) {
+    static int cached[64] = {0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev >= 0 && dev < 64 && cached[dev] > 0) {
+        cus = cached[dev];
+        return hipSuccess;
+    }
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    if (cus <= 0) return hipErrorInvalidValue;
+    if (dev >= 0 && dev < 64) cached[dev] = cus;
+    return hipSuccess;
+}
+
 // ---- sparse aggregation ------------------------------------------------------------
 
 #ifndef LOCO_SA_WG_PER_CU_F32

@@ -221,10 +221,9 @@ hipError_t launch_sa(const SaParams& p, int chunk, int bits, bool out_bf16, hipS
     const int per_cu = out_bf16 ? kSaWgPerCuBf16 : kSaWgPerCuF32;
     int64_t grid = kMaxGrid;
     if (per_cu > 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return hipErrorInvalidValue;
+        int cus = 0;
+        const hipError_t err = compute_units(cus);
+        if (err != hipSuccess) return err;
         grid = (int64_t)cus * per_cu;
     }
     // chunks [c0, c1) per launch: one chunk per workgroup, or all of them for a persistent grid
