@@ -8,9 +8,10 @@
 // (Sec. 3.2, Eqn. (7): e = e8 * fl(1/s_e) on load, e8' = clamp(rint(e' * s_e)) on store),
 // and a step may store e' = 0 instead (the periodic reset of Eqn. (7)).
 //
-// Mapping: a wavefront owns a tile of kCqUnroll sub-tiles of 512 elements; lane l owns
-// 8 consecutive elements of each sub-tile, so one bf16 gradient load, two fp32 error
-// loads and one 32-bit code store per lane are 16-byte (or 4-byte) coalesced accesses.
+// Mapping: a wavefront owns a tile of sub-tiles of 512 elements (one sub-tile with a
+// float error, four with an 8-bit error, whose waves move fewer bytes); lane l owns 8
+// consecutive elements of each sub-tile, so one bf16 gradient load, two fp32 error loads
+// (one 8-byte load of an 8-bit error) and one 32-bit code store per lane are coalesced.
 // A scale block of B elements is B/8 consecutive lanes; its absmax is reduced with DPP
 // row operations (and a permlane swap past 16 lanes).  Every load of a tile is issued
 // before any arithmetic.  The grid covers all wave tiles of all segments of the call:

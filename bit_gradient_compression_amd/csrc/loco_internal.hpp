@@ -135,7 +135,7 @@ hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, int mod
 // Candidate list capacity of the fast selection path.
 constexpr int kTkCap = 512;
 
-// Workgroups of one Top-k launch (one 64-lane workgroup per chunk at a time).
+// Workgroups of one Top-k launch (one 256-thread workgroup per chunk at a time).
 constexpr int64_t kTkMaxGrid = 1 << 20;
 
 struct TkParams {

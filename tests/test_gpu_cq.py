@@ -252,3 +252,43 @@ def test_cq_i8_llama_layer_scaled(gpu_lib):
     say(f"cq i8 llama layer /64: {sizes}")
     run_chain(gpu_lib, sizes, "bf16", "i8", 4, 128, 0.9, 6,
               gen=lambda s, n: torch.cat(W.llama_layer_grads(s, div=64)), err_scale=2.0 ** 18, reset_every=4)
+
+
+@pytest.mark.parametrize("ed", ["f32", "bf16", "i8"])
+def test_cq_teacher_forced(gpu_lib, ed):
+    """Teacher-forced chain: before every step the GPU's error buffer is overwritten with
+    the oracle's, so each step is compared from the same state (no compounding)."""
+    n, bits, block, s_e = 300_007, 4, 128, 2.0 ** 17
+    say(f"cq teacher-forced, {ed} error")
+    g = Guarded(n, torch.bfloat16)
+    e = Guarded(n, TD[ed], init=torch.zeros(n, dtype=TD[ed]))
+    c = Guarded(gpu_lib.code_bytes(n, bits), torch.uint8)
+    a = Guarded(gpu_lib.num_blocks(n, block), torch.float32)
+    e_ora = np.zeros(n, ORA_E[ed])
+    for step in range(4):
+        x = grads(step, n, "bf16", "teacher")
+        g.t.copy_(x)
+        if ed == "bf16":
+            e.t.copy_(torch.from_numpy(e_ora.view(np.int16)).view(torch.bfloat16))
+        else:
+            e.t.copy_(torch.from_numpy(e_ora))
+        gpu_lib.loco_compensate_quantize_ex([(g.t, e.t, c.t, a.t)], bits=bits, block=block, beta=0.9,
+                                            err_scale=s_e if ed == "i8" else 0.0)
+        torch.cuda.synchronize()
+        ref = oracle.compensate_quantize(storage(x, "bf16"), e_ora, bits=bits, block=block, beta=0.9,
+                                         grad_dtype="bf16", err_dtype=ed, err_scale=s_e if ed == "i8" else 0.0)
+        tag = f"teacher-forced step {step}"
+        assert_bytes_equal(host(c.t), ref["codes"], f"{tag} codes")
+        assert_bytes_equal(host(a.t).view(np.uint32), ref["absmax"].view(np.uint32), f"{tag} absmax")
+        if ed == "i8":
+            assert_bytes_equal(host(e.t), ref["e_new"], f"{tag} error")
+        elif ed == "bf16":
+            assert_bf16_close(bf16_bits(e.t), ref["e_new"], f"{tag} error")
+        else:
+            assert_f32_close(host(e.t), ref["e_new"], step_per_elem(ref["absmax"], bits, block, n), f"{tag} error")
+        # the next step starts from a perturbed oracle state, not from the GPU's
+        e_ora = ref["e_new"].copy()
+        if ed == "f32":
+            e_ora[::7] = np.float32(1e-4)
+        for b, nm in ((g, "grad"), (e, "err"), (c, "codes"), (a, "absmax")):
+            b.check(f"{tag} {nm}")

@@ -108,3 +108,30 @@ def test_tk_small_tail_only(gpu_lib):
     for n in (1, 5, 63, 64, 65, 300):
         say(f"tk small n={n}")
         run_tk_chain(gpu_lib, n, 256, 100, 2, 1.0, 2, sparse_gen, f"small n{n}")
+
+
+def test_tk_teacher_forced(gpu_lib):
+    """Teacher-forced: each step starts from the oracle's error (perturbed), not the GPU's."""
+    n, C, k = 9 * 4096 + 333, 4096, 82
+    chunks = -(-n // C)
+    g = Guarded(n, torch.float32)
+    e = Guarded(n, torch.float32)
+    idx = Guarded(chunks * k, torch.int16)
+    codes = Guarded(chunks * gpu_lib.code_bytes(k, 2), torch.uint8)
+    am = Guarded(chunks, torch.float32)
+    e_ora = np.zeros(n, np.float32)
+    for step in range(4):
+        x = W.sparseloco_grad(step, n=n)
+        g.t.copy_(x)
+        e.t.copy_(torch.from_numpy(e_ora))
+        gpu_lib.loco_topk_quantize(g.t, e.t, chunk=C, k=k, idx=idx.t, codes=codes.t, absmax=am.t, bits=2,
+                                   ef_decay=0.9)
+        torch.cuda.synchronize()
+        ref = oracle.topk_quantize(x.numpy(), e_ora, chunk=C, k=k, bits=2, decay=0.9)
+        t = f"tk teacher-forced step {step}"
+        assert_bytes_equal(host(idx.t).view(np.uint16), ref["idx"], f"{t} idx")
+        assert_bytes_equal(host(codes.t), ref["codes"], f"{t} codes")
+        assert_bytes_equal(host(am.t).view(np.uint32), ref["absmax"].view(np.uint32), f"{t} absmax")
+        assert_f32_close(host(e.t), ref["e_new"], np.repeat(ref["absmax"], C)[:n].astype(np.float64), f"{t} error")
+        e_ora = ref["e_new"].copy()
+        e_ora[::11] *= np.float32(0.5)
