@@ -40,6 +40,7 @@ TK_CHUNK, TK_K = 4096, 82
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard.json")
 CSRC = os.path.join(ROOT, "bit_gradient_compression_amd", "csrc")
 KERNEL_FILES = {"compensate_quantize_4bit": ["cq.hip"], "dequant_reduce_8peers": ["dr.hip"],
+                "compensate_quantize_8bit_7b_shard": ["cq.hip"], "compensate_quantize_4bit_i8err_7b_shard": ["cq.hip"],
                 "dequant_reduce_adam_8peers": ["dr.hip"],
                 "sparseloco_topk_2bit": ["tk.hip"], "sparseloco_aggregate_8peers": ["sa.hip"]}
 COMMON_FILES = ["loco_device.hpp", "loco_internal.hpp"]
@@ -318,6 +319,11 @@ def main():
                                                 "GBps": round(bs / ms / 1e6, 1),
                                                 "frac_hbm": round(bs / ms / 1e6 / HBM_PEAK_GBPS, 4)}
         del spays, sout
+
+    for k, v in measured.items():
+        if k in modes:
+            modes[k]["hbm_bytes_measured"] = v["hbm_bytes"]
+            modes[k]["hbm_over_alg"] = round(v["hbm_bytes"] / modes[k]["alg_bytes"], 4)
 
     cpu = None
     if args.cpu_sample > 0:
