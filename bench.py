@@ -6,7 +6,8 @@ A step is one pass of the rank's path on the 7B FSDP-shard workload:
   destination, blocks restarting per partition), then
   dequant-reduce of the 8 peer payloads of the rank's own partition into bf16 (x 1/8).
 Inputs are resident in HBM before the timed region; the error buffer carries over from
-step to step.  The SparseLoCo-style Top-k mode (2^28 fp32, chunk 4096, k = 82, 2-bit),
+step to step.  Compensate-quantize on the LLaMA-7B layer and MoE-expert workloads, the
+SparseLoCo-style Top-k mode (2^28 fp32, chunk 4096, k = 82, 2-bit),
 its sparse aggregation of 8 peers' payloads, the 8-bit-code variant, the 8-bit-error
 variant (LoCo Eqn. (7)) and dequant-reduce fused with the LoCo-Adam step (Eqn. (9)) are
 timed in the same run and reported under "modes".
@@ -41,6 +42,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard.json")
 CSRC = os.path.join(ROOT, "bit_gradient_compression_amd", "csrc")
 KERNEL_FILES = {"compensate_quantize_4bit": ["cq.hip"], "dequant_reduce_8peers": ["dr.hip"],
                 "compensate_quantize_8bit_7b_shard": ["cq.hip"], "compensate_quantize_4bit_i8err_7b_shard": ["cq.hip"],
+                "compensate_quantize_4bit_llama_layer": ["cq.hip"], "compensate_quantize_4bit_moe": ["cq.hip"],
                 "dequant_reduce_adam_8peers": ["dr.hip"],
                 "sparseloco_topk_2bit": ["tk.hip"], "sparseloco_aggregate_8peers": ["sa.hip"]}
 COMMON_FILES = ["loco_device.hpp", "loco_internal.hpp"]
@@ -258,6 +260,23 @@ def main():
                                                       "frac_hbm": round(b8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                                       "grad_GBps": round(n * 2 / ms / 1e6, 1)}
         del codes8, e8, segs8
+        # the LLaMA-7B layer (7 bf16 gradients as 7 segments, fp32 error) and the MoE experts
+        # (24 bf16 matrices with 30% zero rows, bf16 error): 4-bit, block 128
+        for name, grads_of, edt in (("llama_layer", lambda: W.llama_layer_grads(0, device=dev), torch.float32),
+                                    ("moe", lambda: W.moe_grads(0, device=dev), torch.bfloat16)):
+            xg = grads_of()
+            xs = [t.numel() for t in xg]
+            xsegs = [(t, torch.zeros(m, dtype=edt, device=dev), torch.empty((m * 4 + 7) // 8, dtype=torch.uint8,
+                      device=dev), torch.empty(-(-m // 128), device=dev)) for t, m in zip(xg, xs)]
+            ms = timed(lambda: loco.loco_compensate_quantize(xsegs, bits=4, block=128, beta=BETA, stream=stream),
+                       stream, max(10, args.steps // 2))
+            bx = cq_bytes(xs, 2, 2 if edt == torch.bfloat16 else 4, 4, 128)
+            modes[f"compensate_quantize_4bit_{name}"] = {
+                "workload": f"{sum(xs):,} bf16 in {len(xs)} segments, {'bf16' if edt == torch.bfloat16 else 'fp32'} "
+                            "error, 4-bit, block 128",
+                "avg_ms": round(ms, 4), **spread(), "alg_bytes": bx, "GBps": round(bx / ms / 1e6, 1),
+                "frac_hbm": round(bx / ms / 1e6 / HBM_PEAK_GBPS, 4), "grad_GBps": round(sum(xs) * 2 / ms / 1e6, 1)}
+            del xg, xsegs
         # the paper's 8-bit error (LoCo Eqn. (7), s_e = 2^17) with 4-bit codes, same shard
         ei8 = torch.zeros(n, dtype=torch.int8, device=dev)
         segs_i8 = [(g[i * part:(i + 1) * part], ei8[i * part:(i + 1) * part], *segs[i][2:]) for i in range(PARTS)]
