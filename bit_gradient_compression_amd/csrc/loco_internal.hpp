@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace loco {
 
 // ---- compensate-quantize -----------------------------------------------------------
@@ -153,19 +155,24 @@ hipError_t launch_tk(const TkParams& p, int chunk, int bits, hipStream_t stream)
 
 // Compute units of the current device, queried once per device and kept (so launches that
 // size a persistent grid make no device query while a caller captures a graph).
+// Thread-safe: concurrent first calls store the same value.
 inline hipError_t compute_units(int& cus) {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    if (dev >= 0 && dev < 64 && cached[dev] > 0) {
-        cus = cached[dev];
-        return hipSuccess;
+    const bool cacheable = dev >= 0 && dev < 64;
+    if (cacheable) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            cus = c;
+            return hipSuccess;
+        }
     }
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     if (cus <= 0) return hipErrorInvalidValue;
-    if (dev >= 0 && dev < 64) cached[dev] = cus;
+    if (cacheable) cached[dev].store(cus, std::memory_order_relaxed);
     return hipSuccess;
 }
 
