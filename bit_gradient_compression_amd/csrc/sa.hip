@@ -9,16 +9,16 @@
 //   acc[c*C + idx_p[c][j]] += q_p[c][j] * step_p[c],   step = absmax / qmax
 // and out = acc * out_scale; elements that no peer names are 0.
 //
-// Mapping: one workgroup of NT threads per chunk at a time; a persistent grid of a few
-// workgroups per compute unit walks the chunks, loading each chunk's payload while it
-// processes the previous one.  The chunk's fp32 accumulator lives in LDS (C floats, 16 KB
-// at C = 4096) and is zeroed first.
-// Thread t owns slots t, t+NT, ... of every peer.  The first slot of a batch of peers is
-// loaded into registers in one go (all loads in flight together); then the peers are
-// applied one at a time with a barrier between them, so every element adds its
-// contributions in peer order.  Within one peer the slots name distinct elements, so
-// their read-add-writes never collide.  The dense chunk is then written once, each
-// thread storing whole runs of up to 8 outputs.
+// Mapping: one workgroup of NT threads per chunk at a time.  The chunk's fp32 accumulator
+// lives in LDS (C floats, 16 KB at C = 4096) and is zeroed first.  Thread t owns slots t,
+// t+NT, ... of every peer.  The first slot of a batch of peers is loaded into registers in
+// one go (all loads in flight together); then the peers are applied one at a time with a
+// barrier between them, so every element adds its contributions in peer order.  Within
+// one peer the slots name distinct elements, so their read-add-writes never collide.  The
+// dense chunk is then written once, each thread storing whole runs of up to 8 outputs.
+// Two kernels: a streaming one (k <= NT, at most kSaPeerBatch peers: the usual case), a
+// persistent grid of a few workgroups per compute unit that loads each chunk's payload
+// while it processes the previous chunk; and a general one, one workgroup per chunk.
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"
@@ -71,88 +71,90 @@ __device__ __forceinline__ void apply_slot(float* acc, uint32_t ix, uint32_t wor
     }
 }
 
-template <int C, int BITS, bool OBF, int NT, bool PERSIST>
-__global__ __launch_bounds__(NT) void sa_kernel(SaParams p, int64_t c0, int64_t c1) {
-    static_assert(C % NT == 0, "a chunk is a whole number of thread rows");
-    constexpr int QMAX = (1 << (BITS - 1)) - 1;
+// The steps of one chunk, shared by both kernels below.  Thread t owns slot t of every
+// peer (and t + NT, ... in the general kernel when k > NT).
+template <int C, int BITS, bool OBF, int NT>
+struct SaChunk {
+    static constexpr int QMAX = (1 << (BITS - 1)) - 1;
     // outputs per thread per store: 16 bytes (4 fp32 or 8 bf16), so each store instruction
     // of a wave writes one contiguous 1 KB row
-    constexpr int VMAX = OBF ? 8 : LOCO_SA_VEC_F32;
-    constexpr int VEC = C / NT >= VMAX ? VMAX : C / NT;
-    constexpr int GROUPS = C / (NT * VEC);
-    __shared__ __attribute__((aligned(16))) float acc[C];
-    const int t = threadIdx.x;
-    const int lane = lane_id();
-    const int k = p.k;
-    const int shift0 = (t * BITS) % 8;
-    const int ts = t < k ? t : k - 1;  // threads past k re-read slot k-1 and drop it
+    static constexpr int VMAX = OBF ? 8 : LOCO_SA_VEC_F32;
+    static constexpr int VEC = C / NT >= VMAX ? VMAX : C / NT;
+    static constexpr int GROUPS = C / (NT * VEC);
+    static_assert(C % NT == 0, "a chunk is a whole number of thread rows");
 
-    // Slot t of a batch of peers for chunk c, loaded without branches so that every pointer
-    // and load is issued back to back: per peer a uniform chunk pointer, and one lane offset
-    // shared by all peers.  The batch's scales are uniform loads; lane b keeps peer b's and
-    // divides it later (one division per lane), and readlane returns the steps.
-    auto load_batch = [&](int64_t c, int p0, uint32_t (&ix)[kSaPeerBatch], uint32_t (&cw)[kSaPeerBatch],
-                          float& am_mine) {
-        SaPeerDev pe[kSaPeerBatch];
-#pragma unroll
-        for (int b = 0; b < kSaPeerBatch; ++b) pe[b] = p.peer[p0 + b < p.npeers ? p0 + b : p.npeers - 1];
-        const uint32_t io = (uint32_t)ts, co = (uint32_t)(ts * BITS) / 8u;
+    // Slot t of a batch of kSaPeerBatch peers for one chunk.
+    struct Batch {
+        uint32_t ix[kSaPeerBatch], cw[kSaPeerBatch];
         float am[kSaPeerBatch];
-#pragma unroll
-        for (int b = 0; b < kSaPeerBatch; ++b) {
-            am[b] = pe[b].absmax[c];
-            ix[b] = (pe[b].idx + c * k)[io];
-            cw[b] = (pe[b].codes + c * p.cbytes)[co];
-        }
-        am_mine = 0.0f;
-#pragma unroll
-        for (int b = 0; b < kSaPeerBatch; ++b) {
-            am_mine = (lane == b) ? am[b] : am_mine;
-            ix[b] = t < k ? ix[b] : 0xFFFFu;
-        }
     };
 
-    // workgroup w takes chunks c0 + w, c0 + w + gridDim.x, ... below c1; with a persistent
-    // grid the next chunk's first batch is loaded while this one is processed
-    int64_t c = c0 + xcd_remap<kXcds, kSaXcdRun>(blockIdx.x, gridDim.x);
-    if (c >= c1) return;
-    uint32_t ix[kSaPeerBatch], cw[kSaPeerBatch];
-    float am_mine;
-    load_batch(c, 0, ix, cw, am_mine);
-    for (;;) {
-        const int64_t cn = c + gridDim.x;
-        const bool more = cn < c1;  // uniform
-        uint32_t nix[kSaPeerBatch], ncw[kSaPeerBatch];
-        float nam = 0.0f;
-        if constexpr (PERSIST) {
-            if (more && p.npeers <= kSaPeerBatch) load_batch(cn, 0, nix, ncw, nam);
-        }
-        const int64_t base = c * C;
-        const int len = (int)(p.n - base < C ? p.n - base : C);
-#pragma unroll
-        for (int i = t * 4; i < C; i += NT * 4) *(f32x4*)&acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        __syncthreads();
+    const SaParams& p;
+    float* acc;
+    int t, lane, k, shift0;
+    uint32_t io, co;  // this thread's slot and code-byte offsets inside a chunk's payload
 
-        for (int p0 = 0; p0 < p.npeers; p0 += kSaPeerBatch) {
-            if (p0 > 0) load_batch(c, p0, ix, cw, am_mine);
-            const float step_mine = am_mine / (float)QMAX;  // 0 for an all-zero chunk
+    __device__ SaChunk(const SaParams& p_, float* acc_) : p(p_), acc(acc_) {
+        t = threadIdx.x;
+        lane = lane_id();
+        k = p.k;
+        shift0 = (t * BITS) % 8;
+        const int ts = t < k ? t : k - 1;  // threads past k re-read slot k-1 and drop it
+        io = (uint32_t)ts;
+        co = (uint32_t)(ts * BITS) / 8u;
+    }
+
+    // Loads without branches, so every load is issued back to back: per peer a uniform
+    // chunk pointer, and one lane offset shared by all peers.  The loads only fill
+    // registers: nothing reads them until the batch is applied.
+    __device__ __forceinline__ void load(int64_t c, int p0, Batch& B) const {
 #pragma unroll
-            for (int b = 0; b < kSaPeerBatch; ++b) {
-                if (p0 + b < p.npeers) {  // uniform: the barrier below is reached by all threads
-                    const float step =
-                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, step_mine), b));
-                    apply_slot<BITS>(acc, ix[b], cw[b], shift0, step, len);
-                    if (k > NT) {  // slots past the first row, loaded where used
-                        const SaPeerDev pe = p.peer[p0 + b];
-                        for (int j = t + NT; j < k; j += NT)
-                            apply_slot<BITS>(acc, pe.idx[c * k + j], pe.codes[c * p.cbytes + (j * BITS) / 8],
-                                             (j * BITS) % 8, step, len);
-                    }
-                    __syncthreads();
+        for (int b = 0; b < kSaPeerBatch; ++b) {
+            const SaPeerDev pe = p.peer[p0 + b < p.npeers ? p0 + b : p.npeers - 1];
+            B.am[b] = pe.absmax[c];
+            B.ix[b] = (pe.idx + c * k)[io];
+            B.cw[b] = (pe.codes + c * p.cbytes)[co];
+        }
+    }
+
+    __device__ __forceinline__ void clear() const {
+        constexpr int V4 = C / 4;  // 16-byte words per chunk
+#pragma unroll
+        for (int j = 0; j < (V4 + NT - 1) / NT; ++j) {
+            const int i = j * NT + t;
+            if (V4 % NT == 0 || i < V4) *(f32x4*)&acc[i * 4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+
+    // Adds the batch of peers p0.. to the accumulator, one peer at a time with a barrier
+    // after each.  Lane b keeps peer b's scale and divides it (one division per lane);
+    // readlane hands each step to every lane.  An all-zero chunk has step 0.  WIDE: slots
+    // past the first row (k > NT), loaded where used.
+    template <bool WIDE>
+    __device__ __forceinline__ void apply(int64_t c, int p0, const Batch& B, int len) const {
+        float am_mine = 0.0f;
+#pragma unroll
+        for (int b = 0; b < kSaPeerBatch; ++b) am_mine = (lane == b) ? B.am[b] : am_mine;
+        const float step_mine = am_mine / (float)QMAX;
+#pragma unroll
+        for (int b = 0; b < kSaPeerBatch; ++b) {
+            if (p0 + b < p.npeers) {  // uniform: the barrier below is reached by all threads
+                const float step =
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, step_mine), b));
+                apply_slot<BITS>(acc, t < k ? B.ix[b] : 0xFFFFu, B.cw[b], shift0, step, len);
+                if constexpr (WIDE) {
+                    const SaPeerDev pe = p.peer[p0 + b];
+                    for (int j = t + NT; j < k; j += NT)
+                        apply_slot<BITS>(acc, pe.idx[c * k + j], pe.codes[c * p.cbytes + (j * BITS) / 8],
+                                         (j * BITS) % 8, step, len);
                 }
+                __syncthreads();
             }
         }
+    }
 
+    // out[base + i] = acc[i] * out_scale for the chunk's len elements
+    __device__ __forceinline__ void store(int64_t base, int len) const {
         const float scale = p.out_scale;
         if (len == C) {
 #pragma unroll
@@ -169,68 +171,141 @@ __global__ __launch_bounds__(NT) void sa_kernel(SaParams p, int64_t c0, int64_t 
                 store_vec<1, OBF>(p.out, base + i, v);
             }
         }
-        if (!more) break;
-        __syncthreads();  // the next chunk clears acc
-        c = cn;
-        if (PERSIST && p.npeers <= kSaPeerBatch) {
-#pragma unroll
-            for (int b = 0; b < kSaPeerBatch; ++b) {
-                ix[b] = nix[b];
-                cw[b] = ncw[b];
-            }
-            am_mine = nam;
-        } else {
-            load_batch(c, 0, ix, cw, am_mine);
+    }
+
+    // One chunk, any k, any number of peers, possibly short: every batch is loaded where
+    // it is applied.
+    __device__ void whole(int64_t c) const {
+        const int64_t base = c * C;
+        const int len = (int)(p.n - base < C ? p.n - base : C);
+        clear();
+        __syncthreads();
+        for (int p0 = 0; p0 < p.npeers; p0 += kSaPeerBatch) {
+            Batch B;
+            load(c, p0, B);
+            apply<true>(c, p0, B, len);
         }
+        store(base, len);
+    }
+};
+
+// Makes the compiler treat the batch's registers as redefined here: it waits for their
+// loads at this point, and later uses need no wait.
+template <class Batch>
+__device__ __forceinline__ void settle(Batch& B) {
+#pragma unroll
+    for (int b = 0; b < kSaPeerBatch; ++b) asm volatile("" : "+v"(B.ix[b]), "+v"(B.cw[b]), "+v"(B.am[b]));
+}
+
+// General kernel: one workgroup per chunk of [c0, c1), any k and number of peers.
+template <int C, int BITS, bool OBF, int NT>
+__global__ __launch_bounds__(NT) void sa_kernel(SaParams p, int64_t c0, int64_t c1) {
+    __shared__ __attribute__((aligned(16))) float acc[C];
+    const SaChunk<C, BITS, OBF, NT> ch(p, acc);
+    for (int64_t c = c0 + xcd_remap<kXcds, kSaXcdRun>(blockIdx.x, gridDim.x); c < c1; c += gridDim.x) {
+        ch.whole(c);
+        __syncthreads();  // the next chunk clears acc
+    }
+}
+
+// Streaming kernel for k <= NT and at most kSaPeerBatch peers: a persistent grid walks
+// the whole chunks, workgroup w taking w, w + gridDim.x, ...  Each step issues the loads
+// of the workgroup's next chunk before it processes the current one, so they are in
+// flight while it does.  Every step runs the same instructions (the loads are issued
+// unconditionally, for the current chunk again on the last step; whole chunks only, so
+// the stores are straight-line), and the next batch is settled at the end of a step,
+// after the stores: the wait for it then leaves those stores in flight.  A short last
+// chunk is done by the last workgroup afterwards.
+template <int C, int BITS, bool OBF, int NT>
+__global__ __launch_bounds__(NT) void sa_stream_kernel(SaParams p) {
+    __shared__ __attribute__((aligned(16))) float acc[C];
+    using Ch = SaChunk<C, BITS, OBF, NT>;
+    const Ch ch(p, acc);
+    const int64_t nfull = p.n / C;
+    int64_t c = xcd_remap<kXcds, kSaXcdRun>(blockIdx.x, gridDim.x);
+    if (c < nfull) {
+        using Batch = typename Ch::Batch;
+        const int64_t G = gridDim.x;
+        Batch cur, nxt;
+        ch.load(c, 0, cur);
+        settle(cur);
+        for (;;) {
+            const int64_t cn = c + G;
+            const bool more = cn < nfull;  // uniform
+            ch.load(more ? cn : c, 0, nxt);
+            ch.clear();
+            __syncthreads();
+            ch.template apply<false>(c, 0, cur, C);
+            ch.store(c * C, C);
+            if (!more) break;
+            __syncthreads();  // the next chunk clears acc
+            c = cn;
+            cur = nxt;
+            settle(cur);
+        }
+    }
+    if (nfull < p.nchunks && blockIdx.x == gridDim.x - 1) {
+        __syncthreads();
+        ch.whole(nfull);
     }
 }
 
 // Launch shape per output type, measured on MI355X for 8 peers of 2^28 in chunks of 4096
-// with the payloads out of the Infinity Cache: 128 threads per chunk and a persistent
-// grid of 6 (fp32) or 8 (bf16) workgroups per compute unit: fp32 0.257 ms against 0.36 ms
-// with one 256-thread workgroup per chunk; bf16 0.171 against 0.213 ms.
+// (payloads out of the Infinity Cache / still in it): 128 threads per chunk; fp32 out with
+// 3 workgroups per compute unit 0.249 / 0.197 ms, against 0.28 / 0.21 with 6 and 0.28 /
+// 0.21 with 2; bf16 out with 8, 0.172 / 0.112 ms.  Loading two chunks ahead instead of one
+// changed nothing: the time goes to the dense writes and their mix with the payload reads,
+// not to waiting for the payloads.
 template <int C, int BITS>
-const void* pick_out(bool out_bf16) {
-    return out_bf16 ? (const void*)&sa_kernel<C, BITS, true, kSaThreadsBf16, (kSaWgPerCuBf16 > 0)>
-                    : (const void*)&sa_kernel<C, BITS, false, kSaThreadsF32, (kSaWgPerCuF32 > 0)>;
+void pick_out(bool out_bf16, bool stream, const void*& k) {
+    if (stream)
+        k = out_bf16 ? (const void*)&sa_stream_kernel<C, BITS, true, kSaThreadsBf16>
+                     : (const void*)&sa_stream_kernel<C, BITS, false, kSaThreadsF32>;
+    else
+        k = out_bf16 ? (const void*)&sa_kernel<C, BITS, true, kSaThreadsBf16>
+                     : (const void*)&sa_kernel<C, BITS, false, kSaThreadsF32>;
 }
 
 template <int C>
-const void* pick_bits(int bits, bool out_bf16) {
+void pick_bits(int bits, bool out_bf16, bool stream, const void*& k) {
     switch (bits) {
-        case 2: return pick_out<C, 2>(out_bf16);
-        case 4: return pick_out<C, 4>(out_bf16);
-        case 8: return pick_out<C, 8>(out_bf16);
+        case 2: pick_out<C, 2>(out_bf16, stream, k); break;
+        case 4: pick_out<C, 4>(out_bf16, stream, k); break;
+        case 8: pick_out<C, 8>(out_bf16, stream, k); break;
     }
-    return nullptr;
 }
 
 }  // namespace
 
 hipError_t launch_sa(const SaParams& p, int chunk, int bits, bool out_bf16, hipStream_t stream) {
-    const void* k = nullptr;
-    switch (chunk) {
-        case 256: k = pick_bits<256>(bits, out_bf16); break;
-        case 512: k = pick_bits<512>(bits, out_bf16); break;
-        case 1024: k = pick_bits<1024>(bits, out_bf16); break;
-        case 2048: k = pick_bits<2048>(bits, out_bf16); break;
-        case 4096: k = pick_bits<4096>(bits, out_bf16); break;
-    }
-    if (!k) return hipErrorInvalidValue;
     const int threads = out_bf16 ? kSaThreadsBf16 : kSaThreadsF32;
     const int per_cu = out_bf16 ? kSaWgPerCuBf16 : kSaWgPerCuF32;
-    int64_t grid = kMaxGrid;
-    if (per_cu > 0) {
+    const bool streaming = per_cu > 0 && p.k <= threads && p.npeers <= kSaPeerBatch;
+    const void* k = nullptr;
+    switch (chunk) {
+        case 256: pick_bits<256>(bits, out_bf16, streaming, k); break;
+        case 512: pick_bits<512>(bits, out_bf16, streaming, k); break;
+        case 1024: pick_bits<1024>(bits, out_bf16, streaming, k); break;
+        case 2048: pick_bits<2048>(bits, out_bf16, streaming, k); break;
+        case 4096: pick_bits<4096>(bits, out_bf16, streaming, k); break;
+    }
+    if (!k) return hipErrorInvalidValue;
+    if (streaming) {
         int cus = 0;
         const hipError_t err = compute_units(cus);
         if (err != hipSuccess) return err;
-        grid = (int64_t)cus * per_cu;
+        // at least one workgroup, at most one per whole chunk (a short last chunk alone
+        // takes one workgroup)
+        const int64_t nfull = p.n / chunk;
+        const int64_t grid = (int64_t)cus * per_cu;
+        const int64_t blocks = nfull < 1 ? 1 : (nfull < grid ? nfull : grid);
+        void* args[] = {(void*)&p};
+        return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
     }
-    // chunks [c0, c1) per launch: one chunk per workgroup, or all of them for a persistent grid
-    const int64_t span = per_cu > 0 ? p.nchunks : kMaxGrid;
-    for (int64_t c0 = 0; c0 < p.nchunks; c0 += span) {
-        int64_t c1 = p.nchunks - c0 < span ? p.nchunks : c0 + span;
-        const int64_t blocks = c1 - c0 < grid ? c1 - c0 : grid;
+    // one workgroup per chunk, chunks [c0, c1) per launch
+    for (int64_t c0 = 0; c0 < p.nchunks; c0 += kMaxGrid) {
+        int64_t c1 = p.nchunks - c0 < kMaxGrid ? p.nchunks : c0 + kMaxGrid;
+        const int64_t blocks = c1 - c0;
         void* args[] = {(void*)&p, (void*)&c0, (void*)&c1};
         const hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
         if (err != hipSuccess) return err;

@@ -101,3 +101,14 @@ def test_sa_deterministic(gpu_lib):
         torch.cuda.synchronize()
         outs.append(host(o))
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("od", ["f32", "bf16"])
+def test_sa_many_chunks_per_workgroup(gpu_lib, od):
+    """More chunks than the persistent grid has workgroups, so each walks several (its
+    next payload loaded while the current chunk is applied), plus a short last chunk."""
+    chunk, k = 256, 82
+    n = chunk * 6000 + 37
+    say(f"sa many chunks per workgroup, n={n}, {od}")
+    peers = [W.random_sparse_payload(n, chunk, k, 4, key=("w", p)) for p in range(8)]
+    check(gpu_lib, peers, n, chunk, k, 4, od, 0.125, f"many chunks {od}")
