@@ -198,8 +198,7 @@ constexpr int kSaThreadsBf16 = LOCO_SA_THREADS_BF16;  // threads per chunk, bf16
 constexpr int kSaPeerBatch = 8;  // peers whose first slot is loaded together
 // Workgroups per compute unit of the persistent grid, per output type: each workgroup
 // takes every gridDim.x-th chunk and loads the next chunk's payload while it processes
-// the current one (0: one workgroup per chunk, no prefetch).  The output is ~92% of the
-// bytes and dense writes run best with few waves in flight, so the fp32 grid is small.
+// the current one (0: one workgroup per chunk, no prefetch).
 constexpr int kSaWgPerCuF32 = LOCO_SA_WG_PER_CU_F32;
 constexpr int kSaWgPerCuBf16 = LOCO_SA_WG_PER_CU_BF16;
 

@@ -222,7 +222,12 @@ __global__ __launch_bounds__(NT) void sa_stream_kernel(SaParams p) {
     using Ch = SaChunk<C, BITS, OBF, NT>;
     const Ch ch(p, acc);
     const int64_t nfull = p.n / C;
-    int64_t c = xcd_remap<kXcds, kSaXcdRun>(blockIdx.x, gridDim.x);
+    // XCD x (dispatch is round-robin over the XCDs) takes the x-th block of gridDim.x / 8
+    // consecutive chunks of every pass, the same on each pass, so chunks whose payloads
+    // share cache lines meet in one L2: the L2s fetch the payloads once (runs of 64 that
+    // change XCD from pass to pass fetched 1.5x, runs of 1 2.5x)
+    const int64_t g = gridDim.x, b = blockIdx.x;
+    int64_t c = g % kXcds == 0 ? (b % kXcds) * (g / kXcds) + b / kXcds : b;
     if (c < nfull) {
         using Batch = typename Ch::Batch;
         const int64_t G = gridDim.x;
@@ -252,9 +257,10 @@ __global__ __launch_bounds__(NT) void sa_stream_kernel(SaParams p) {
 
 // Launch shape per output type, measured on MI355X for 8 peers of 2^28 in chunks of 4096
 // (payloads out of the Infinity Cache / still in it): 128 threads per chunk; fp32 out with
-// 3 workgroups per compute unit 0.249 / 0.197 ms, against 0.28 / 0.21 with 6 and 0.28 /
-// 0.21 with 2; bf16 out with 8, 0.172 / 0.112 ms.  Loading two chunks ahead instead of one
-// changed nothing: the time goes to the dense writes and their mix with the payload reads,
+// 3 workgroups per compute unit 0.254 / 0.207 ms, against 0.28 / 0.21 with 6 and 0.28 /
+// 0.21 with 2; bf16 out with 8, 0.168 / 0.107 ms.  The output is ~92% of the bytes, and
+// dense writes run best with few waves in flight.  Loading two chunks ahead instead of
+// one changed nothing: the time goes to the writes and their mix with the payload reads,
 // not to waiting for the payloads.
 template <int C, int BITS>
 void pick_out(bool out_bf16, bool stream, const void*& k) {
