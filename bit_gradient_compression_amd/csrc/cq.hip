@@ -35,10 +35,18 @@ __device__ __forceinline__ float load1(const void* p, int64_t i, float estep) {
     else return ((const float*)p)[i];
 }
 
+// The int8 error code of x: clamp(rint(x * escale), -128, 127), ties to even, as the low
+// byte of a float's bits.  Clamping before rounding gives the same integer (the bounds are
+// integers), and adding 1.5 * 2^23 to a value in [-128, 127] rounds it to an integer (ties
+// to even) held in the low mantissa bits, two's complement in the low byte.
+__device__ __forceinline__ uint32_t i8_code_bits(float x, float escale) {
+    return __float_as_uint(__builtin_amdgcn_fmed3f(x * escale, -128.0f, 127.0f) + 12582912.0f);
+}
+
 template <int K>
 __device__ __forceinline__ void store1(void* p, int64_t i, float v, float escale) {
     if constexpr (K == kBF16) ((uint16_t*)p)[i] = bf16_rne(v);
-    else if constexpr (K == kI8) ((int8_t*)p)[i] = (int8_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(v * escale), -128.0f, 127.0f);
+    else if constexpr (K == kI8) ((int8_t*)p)[i] = (int8_t)(i8_code_bits(v, escale) & 0xFFu);
     else ((float*)p)[i] = v;
 }
 
@@ -76,24 +84,30 @@ __device__ __forceinline__ void load8(const void* p, int64_t i0, float (&x)[8], 
     }
 }
 
+// 8 consecutive elements of the new error; zero: store 0 instead (the error reset).
 template <int K>
-__device__ __forceinline__ void store8(void* p, int64_t i0, const float (&x)[8], float escale) {
+__device__ __forceinline__ void store8(void* p, int64_t i0, const float (&x)[8], float escale, bool zero) {
     if constexpr (K == kBF16) {
         u32x4 w;
         w.x = bf16x2_rne(x[0], x[1]); w.y = bf16x2_rne(x[2], x[3]);
         w.z = bf16x2_rne(x[4], x[5]); w.w = bf16x2_rne(x[6], x[7]);
+        if (zero) w = u32x4{0u, 0u, 0u, 0u};
         __builtin_nontemporal_store(w, (u32x4*)((uint16_t*)p + i0));
     } else if constexpr (K == kI8) {
-        uint32_t b[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            b[j] = (uint32_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(x[j] * escale), -128.0f, 127.0f) & 0xFFu;
-        const u32x2 w = {b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24};
+        u32x2 w = {low_bytes4(i8_code_bits(x[0], escale), i8_code_bits(x[1], escale), i8_code_bits(x[2], escale),
+                              i8_code_bits(x[3], escale)),
+                   low_bytes4(i8_code_bits(x[4], escale), i8_code_bits(x[5], escale), i8_code_bits(x[6], escale),
+                              i8_code_bits(x[7], escale))};
+        if (zero) w = u32x2{0u, 0u};
         __builtin_nontemporal_store(w, (u32x2*)((int8_t*)p + i0));
     } else {
         f32x4* q = (f32x4*)((float*)p + i0);
         f32x4 a = {x[0], x[1], x[2], x[3]};
         f32x4 b = {x[4], x[5], x[6], x[7]};
+        if (zero) {
+            a = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            b = a;
+        }
         __builtin_nontemporal_store(a, q);
         __builtin_nontemporal_store(b, q + 1);
     }
@@ -137,40 +151,32 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
             step = p.fixed_step;
             inv = p.fixed_inv;
         } else {
-            uint32_t m = 0;
+            // max |h| as a float (|x| is a free source modifier): for finite values the
+            // same element, and the same bits, as the largest |h| bit pattern
+            float mf = 0.0f;
 #pragma unroll
-            for (int j = 0; j < kCqVec; ++j) m = max(m, __float_as_uint(h[u][j]) & 0x7FFFFFFFu);
-            m = group_max_u32<LPB>(m);
+            for (int j = 0; j < kCqVec; ++j) mf = fmaxf(mf, fabsf(h[u][j]));
+            uint32_t m = group_max_u32<LPB>(__float_as_uint(mf));
             am = __uint_as_float(m);
             step = am / (float)QMAX;
             inv = (m != 0u) ? 1.0f / step : 0.0f;
         }
 
-        float en[kCqVec];
-        uint32_t packed_lo = 0, packed_hi = 0;
+        float en[kCqVec], rq[kCqVec];
 #pragma unroll
         for (int j = 0; j < kCqVec; ++j) {
             const float x = h[u][j] * inv;
-            const float rq = __builtin_amdgcn_fmed3f(__builtin_rintf(x), (float)(-QMAX - 1), (float)QMAX);
-            const int q = (int)rq;
-            const float d = (float)q * step;                     // decompressor
+            rq[j] = __builtin_amdgcn_fmed3f(__builtin_rintf(x), (float)(-QMAX - 1), (float)QMAX);
+            const float d = rq[j] * step;                        // decompressor (rq is the integer q)
             const float r = h[u][j] - d;                         // Eqn. (4)
             en[j] = p.beta * e[u][j] + p.omega * r;              // Eqn. (5)
-            const uint32_t f = (uint32_t)q & ((1u << BITS) - 1u);
-            if constexpr (BITS == 8) {
-                if (j < 4) packed_lo |= f << (8 * j);
-                else packed_hi |= f << (8 * (j - 4));
-            } else {
-                packed_lo |= f << (BITS * j);
-            }
         }
-        if (p.reset) {  // Eqn. (7): this step stores a zero error
-#pragma unroll
-            for (int j = 0; j < kCqVec; ++j) en[j] = 0.0f;
-        }
+        uint32_t packed_lo, packed_hi;
+        pack_codes8<BITS>(rq, packed_lo, packed_hi);
+        const bool zero = p.reset;  // Eqn. (7): this step stores a zero error
 
         if constexpr (FULL) {
-            store8<EK>(sg.e, i0, en, p.err_scale);
+            store8<EK>(sg.e, i0, en, p.err_scale, zero);
             uint8_t* c = sg.codes + (i0 * BITS) / 8;
             if constexpr (BITS == 8) {
                 u32x2 w = {packed_lo, packed_hi};
@@ -188,7 +194,7 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
             const int nvalid = left <= 0 ? 0 : (left >= kCqVec ? kCqVec : (int)left);
 #pragma unroll
             for (int j = 0; j < kCqVec; ++j)
-                if (j < nvalid) store1<EK>(sg.e, i0 + j, en[j], p.err_scale);
+                if (j < nvalid) store1<EK>(sg.e, i0 + j, zero ? 0.0f : en[j], p.err_scale);
             const int nbytes = (nvalid * BITS + 7) / 8;
             uint8_t* c = sg.codes + (i0 * BITS) / 8;
 #pragma unroll

@@ -43,6 +43,56 @@ __device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
     return r;
 }
 
+// ---- code packing -----------------------------------------------------------------
+
+// Eight BITS-bit two's-complement codes q[j] (integer-valued floats in [-2^(BITS-1),
+// 2^(BITS-1) - 1]) packed in element order: code j in bits [BITS*j, BITS*j + BITS) of the
+// 8*BITS-bit result (lo: bits 0-31, hi: bits 32-63).  Each byte is formed as an exact float
+// sum of the biased codes q + 2^(BITS-1) (in [0, 2^BITS)), put in its byte by
+// v_cvt_pk_u8_f32, and one xor per word turns every biased field back into the code
+// (within a BITS-bit field, q + 2^(BITS-1) == q ^ 2^(BITS-1) mod 2^BITS).
+template <int BITS>
+__device__ __forceinline__ void pack_codes8(const float (&q)[8], uint32_t& lo, uint32_t& hi) {
+    lo = 0u;
+    hi = 0u;
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo = __builtin_amdgcn_cvt_pk_u8_f32(q[j] + 128.0f, j, lo);
+            hi = __builtin_amdgcn_cvt_pk_u8_f32(q[4 + j] + 128.0f, j, hi);
+        }
+        lo ^= 0x80808080u;
+        hi ^= 0x80808080u;
+    } else if constexpr (BITS == 4) {
+        // byte b holds codes 2b (low nibble) and 2b+1: (q0 + 8) + 16 (q1 + 8)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            lo = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[2 * b + 1], 16.0f, q[2 * b] + 136.0f), b, lo);
+        lo ^= 0x88888888u;
+    } else {
+        static_assert(BITS == 2, "2, 4 or 8 bits");
+        // byte b holds codes 4b..4b+3: sum of (q_i + 2) 4^i
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float v = q[4 * b] + 170.0f;
+            v = __builtin_fmaf(q[4 * b + 1], 4.0f, v);
+            v = __builtin_fmaf(q[4 * b + 2], 16.0f, v);
+            v = __builtin_fmaf(q[4 * b + 3], 64.0f, v);
+            lo = __builtin_amdgcn_cvt_pk_u8_f32(v, b, lo);
+        }
+        lo ^= 0xAAAAu;
+    }
+}
+
+// Low bytes of four words, in order: b0's low byte in bits 0-7 ... b3's in bits 24-31.
+__device__ __forceinline__ uint32_t low_bytes4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    // v_perm_b32: selector byte values 0-3 pick bytes of the second operand, 4-7 of the
+    // first, 0x0c gives zero
+    const uint32_t t01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t t23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+}
+
 // ---- wavefront primitives -------------------------------------------------------
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

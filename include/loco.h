@@ -104,6 +104,8 @@ typedef struct {
  *   block       64, 128, 256 or 512 (ignored when fixed_scale > 0)
  *   beta        in [0, 1]
  *   fixed_scale 0 for per-block absmax scales, or a finite s > 0
+ * g and e must be finite, and so must h = g + e; for NaN or infinite values the codes,
+ * scales and error are unspecified (no fault).
  * Any number of segments is accepted (they are launched 32 at a time, in order).
  * err_dtype LOCO_I8 is refused here (LOCO_ERR_INVALID): it needs the error scale of
  * loco_compensate_quantize_ex.
