@@ -143,24 +143,59 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
         for (int j = 0; j < kCqVec; ++j) h[u][j] = g[j] + e[u][j];  // Eqn. (2)
     }
 
+    // Block scales.  With several sub-tiles per wave, lane b takes the maximum of the
+    // tile's b-th block and divides once (step = absmax / qmax, inv = 1 / step); each lane
+    // then fetches its own block's pair: the same quotients, one division per block
+    // instead of one per lane.
+    constexpr int BPS = 64 / LPB;  // blocks per sub-tile
+    float step_u[U], inv_u[U], am_u[U];
+    if constexpr (FIXED) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t i0 = base + u * SUB + lane * kCqVec;
-        float step, inv, am = 0.0f;
-        if constexpr (FIXED) {
-            step = p.fixed_step;
-            inv = p.fixed_inv;
-        } else {
+        for (int u = 0; u < U; ++u) {
+            step_u[u] = p.fixed_step;
+            inv_u[u] = p.fixed_inv;
+            am_u[u] = 0.0f;
+        }
+    } else {
+        uint32_t mu[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             // max |h| as a float (|x| is a free source modifier): for finite values the
             // same element, and the same bits, as the largest |h| bit pattern
             float mf = 0.0f;
 #pragma unroll
             for (int j = 0; j < kCqVec; ++j) mf = fmaxf(mf, fabsf(h[u][j]));
-            uint32_t m = group_max_u32<LPB>(__float_as_uint(mf));
-            am = __uint_as_float(m);
-            step = am / (float)QMAX;
-            inv = (m != 0u) ? 1.0f / step : 0.0f;
+            mu[u] = group_max_u32<LPB>(__float_as_uint(mf));
+            am_u[u] = __uint_as_float(mu[u]);
         }
+        if constexpr (U > 1) {
+            uint32_t mb = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t v = (uint32_t)__shfl((int)mu[u], (lane % BPS) * LPB, 64);
+                mb = (lane / BPS == u) ? v : mb;
+            }
+            const float stepb = __uint_as_float(mb) / (float)QMAX;
+            const float invb = (mb != 0u) ? 1.0f / stepb : 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int src = u * BPS + lane / LPB;
+                step_u[u] = __shfl(stepb, src, 64);
+                inv_u[u] = __shfl(invb, src, 64);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                step_u[u] = am_u[u] / (float)QMAX;
+                inv_u[u] = (mu[u] != 0u) ? 1.0f / step_u[u] : 0.0f;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i0 = base + u * SUB + lane * kCqVec;
+        const float step = step_u[u], inv = inv_u[u], am = am_u[u];
 
         float en[kCqVec], rq[kCqVec];
 #pragma unroll
