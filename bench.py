@@ -18,8 +18,10 @@ its time); its GB/s use the slower of the two.
 
 Prints one JSON line.  value = gradient GB/s = 842,000,000 x 2 bytes / step time.
 roofline: the compensate-quantize kernel's algorithmic bytes / its average launch time
-(HIP events on its stream) against 8 TB/s.  cpu_baseline: the CPU oracle on a bounded
-sample of the same workload on this host.
+(HIP events on its stream) against 8 TB/s.  copy_ceiling: a plain 1 GiB streaming copy
+for context; every kernel also reports its GB/s over it (frac_copy).  cpu_baseline: the
+CPU oracle on a bounded sample of the same workload on this host, in one process, and
+(parallel) fanned out over the host's cores.
 """
 
 from __future__ import annotations
@@ -137,6 +139,69 @@ def cpu_baseline(g_dev, payloads_dev, slab, min_seconds=10.0):
                       f"time; NumPy element-wise, one thread ({avail} cores available to the process, {model})"}
 
 
+
+def _oracle_worker(slabs, barrier):
+    """One worker of the parallel oracle timing: the oracle, unchanged, over its slabs
+    (the same two steps per slab as cpu_baseline), started when every worker is ready.
+    Returns its wall-clock span and the gradient elements it covered."""
+    import numpy as np
+
+    import oracle
+    part = slabs[0][0].size // PARTS
+    # untimed warm-up on the first 2^16 elements (first calls into NumPy are slow)
+    g0, pays0 = slabs[0]
+    w = 1 << 16
+    oracle.compensate_quantize(g0[:w], np.zeros(w, np.float32), bits=BITS, block=BLOCK, beta=BETA, grad_dtype="bf16")
+    oracle.dequant_reduce([(c[:(w // PARTS * BITS) // 8], a[:w // PARTS // BLOCK]) for c, a in pays0], w // PARTS,
+                          bits=BITS, block=BLOCK, out_scale=1.0 / PARTS, out_dtype="bf16")
+    barrier.wait()
+    t0 = time.time()
+    for g, pays in slabs:
+        e = np.zeros(g.size, np.float32)
+        for _ in range(2):
+            r = oracle.compensate_quantize(g, e, bits=BITS, block=BLOCK, beta=BETA, grad_dtype="bf16")
+            e = r["e_new"]
+            oracle.dequant_reduce(pays, part, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS, out_dtype="bf16")
+    return t0, time.time(), sum(g.size for g, _ in slabs)
+
+
+def cpu_baseline_parallel(g_dev, payloads_dev, slab, per_worker=4):
+    """The same oracle fanned out over slabs across the host's cores (blocks and slabs are
+    independent, so the results are the ones the single process computes): one spawned
+    process per core (at most 16), each taking `per_worker` consecutive slabs.  Throughput
+    = gradient bytes of all slabs / (2 steps) / the span from the first worker's start
+    to the last one's end."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+
+    import numpy as np
+    import torch
+    workers = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count())
+    n = g_dev.numel()
+    part = slab // PARTS
+    nslab = min(workers * per_worker, n // slab)
+    slabs = []
+    for s in range(nslab):
+        lo = s * slab
+        g = g_dev[lo:lo + slab].cpu().view(torch.int16).numpy().view(np.uint16)
+        off = lo // PARTS
+        pays = [(c[(off * BITS) // 8:((off + part) * BITS + 7) // 8].cpu().numpy(),
+                 a[off // BLOCK:-(-(off + part) // BLOCK)].cpu().numpy()) for c, a in payloads_dev]
+        slabs.append((g, pays))
+    jobs = [slabs[w::workers] for w in range(workers) if slabs[w::workers]]
+    # spawned (not forked) workers: none inherits this process's GPU runtime; a worker that
+    # dies raises here instead of being replaced.  A barrier starts them together, so the
+    # span is their common compute time, not their start-up skew.
+    ctx = multiprocessing.get_context("spawn")
+    with ctx.Manager() as mgr, ProcessPoolExecutor(len(jobs), mp_context=ctx) as pool:
+        barrier = mgr.Barrier(len(jobs), timeout=600)
+        res = list(pool.map(_oracle_worker, jobs, [barrier] * len(jobs)))
+    span = max(r[1] for r in res) - min(r[0] for r in res)
+    elems = sum(r[2] for r in res)
+    return {"value": round(elems * 2 / (span / 2) / 1e9, 4), "unit": "GB/s", "cores": len(jobs),
+            "sample": f"{elems:,} elements in {nslab} slabs of {slab:,}, {per_worker} per process, 2 steps each, "
+                      f"{span:.1f} s from the processes' common start to the last one's end"}
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,7 +211,8 @@ def main():
                     help="slab size of the CPU-oracle baseline (0: skip it)")
     ap.add_argument("--no-modes", action="store_true", help="skip the 8-bit and Top-k modes")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 1 GiB device copy (calibrates the HBM byte counters)")
+                    help="kept for the counter commands: the 1 GiB device copy that calibrates the HBM byte "
+                         "counters now runs on every call")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (peers are simulated "
@@ -190,13 +256,24 @@ def main():
     out = torch.empty(part, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    if args.copy_probe:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    # a plain 1 GiB device copy (its launches calibrate the HBM byte counters), then the
+    # streaming ceiling for context: a 1 GiB read + 1 GiB write through torch's elementwise
+    # kernel (neg into a second buffer), which streams faster than copy_'s blit kernel
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in cevs:
+        a.record(stream)
+        torch.neg(src, out=dst)
+        b.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = sorted(a.elapsed_time(b) for a, b in cevs)[len(cevs) // 2]
+    copy_gbps = 2 * src.numel() * 4 / copy_ms / 1e6
+    del src, dst
 
     def step(evs=None):
         if evs is not None:
@@ -344,10 +421,16 @@ def main():
             modes[k]["hbm_bytes_measured"] = v["hbm_bytes"]
             modes[k]["hbm_over_alg"] = round(v["hbm_bytes"] / modes[k]["alg_bytes"], 4)
 
+    for table in (kernels, modes):
+        for v in table.values():
+            v["frac_copy"] = round(v["GBps"] / copy_gbps, 4)
+
     cpu = None
     if args.cpu_sample > 0:
         log(f"bench: CPU oracle on slabs of {args.cpu_sample:,} elements (>= 10 s)")
         cpu = cpu_baseline(g, payloads, args.cpu_sample)
+        log("bench: the same oracle fanned out over the host's cores")
+        cpu["parallel"] = cpu_baseline_parallel(g, payloads, args.cpu_sample)
 
     value = n * 2 / (ms_per_step / 1e3) / 1e9
     line = {
@@ -364,6 +447,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "compensate_quantize_4bit", "alg_bytes_per_launch": cq_alg},
         "cpu_baseline": cpu,
+        "copy_ceiling": {"GBps": round(copy_gbps, 1), "frac_hbm": round(copy_gbps / HBM_PEAK_GBPS, 4),
+                         "what": "1 GiB read + 1 GiB write streamed by torch.neg(src, out=dst), bytes / median "
+                                 "time of 10; each kernel's frac_copy is its GB/s over this"},
         "kernels": kernels,
         "modes": modes,
         "pct_hbm_peak_step": round(100 * (cq_alg + dr_alg) / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
