@@ -5,6 +5,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "loco.h"
 #include "loco_internal.hpp"
 
@@ -26,6 +29,25 @@ struct Range {
 };
 Range range_of(const void* p, int64_t bytes) { return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
 bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+// True if some written range overlaps any other range (written or read); read-only
+// ranges may overlap each other.  Empty ranges never overlap.  Sorted by start, a range
+// overlaps an earlier one exactly when it starts before the largest end seen so far.
+struct Span {
+    Range r;
+    bool written;
+};
+bool any_write_overlap(std::vector<Span>& v) {
+    std::sort(v.begin(), v.end(), [](const Span& a, const Span& b) { return a.r.lo < b.r.lo; });
+    uintptr_t end_any = 0, end_written = 0;
+    for (const Span& s : v) {
+        if (s.r.lo >= s.r.hi) continue;
+        if (s.r.lo < (s.written ? end_any : end_written)) return true;
+        end_any = std::max(end_any, s.r.hi);
+        if (s.written) end_written = std::max(end_written, s.r.hi);
+    }
+    return false;
+}
 
 int64_t code_bytes(int64_t n, int bits) { return (n * bits + 7) / 8; }
 int64_t nblocks(int64_t n, int block) { return (n + block - 1) / block; }
@@ -95,6 +117,19 @@ int compensate_quantize(const loco_cq_segment_t* segs, int nseg, int grad_dtype,
         ++live;
     }
     if (live == 0) return LOCO_OK;
+    // across segments: no buffer the call writes (any segment's err, codes, absmax) may overlap another
+    // buffer of the call; gradients are only read and may overlap each other
+    std::vector<Span> spans;
+    spans.reserve(4 * live);
+    for (int i = 0; i < nseg; ++i) {
+        const loco_cq_segment_t& s = segs[i];
+        if (s.n == 0) continue;
+        spans.push_back({range_of(s.grad, s.n * gs), false});
+        spans.push_back({range_of(s.err, s.n * es), true});
+        spans.push_back({range_of(s.codes, code_bytes(s.n, bits)), true});
+        if (!fixed) spans.push_back({range_of(s.absmax, nblocks(s.n, block) * 4), true});
+    }
+    if (any_write_overlap(spans)) return LOCO_ERR_INVALID;
 
     CqParams p;
     memset(&p, 0, sizeof(p));

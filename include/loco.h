@@ -74,7 +74,9 @@ typedef enum { LOCO_F32 = 0, LOCO_BF16 = 1, LOCO_I8 = 2 } loco_dtype_t;
  *   absmax  device, ceil(n/block) floats (written): the block's max |h|; unused and
  *           may be NULL when fixed_scale > 0
  *   n       elements (>= 0; 0 is a no-op)
- * The four buffers of a segment must not overlap.
+ * No buffer a call writes (the err, codes and absmax of any of its segments) may
+ * overlap another buffer of the call; gradients are only read and may overlap each
+ * other (LOCO_ERR_INVALID otherwise).
  */
 typedef struct {
     const void* grad;

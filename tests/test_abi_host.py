@@ -120,6 +120,22 @@ def test_cq_noop_and_mixed(lib):
     assert cq(lib, [seg(a=0, g=A + 2)], fixed=2.0 ** 19, block=7) == ALIGN
 
 
+def test_cq_buffers_of_different_segments(lib):
+    """A buffer one segment writes must not overlap any buffer of another segment."""
+    s0 = seg()
+    off = 1 << 20
+    # the second segment's error overlaps the first one's codes (500 bytes at 4 bits)
+    assert cq(lib, [s0, seg(g=A + off, e=Cp + 256, c=Cp + off, a=Dp + off)]) == INV
+    # the second segment's codes overlap the first one's gradient
+    assert cq(lib, [s0, seg(g=A + off, e=Bp + off, c=A + 64, a=Dp + off)]) == INV
+    # the second segment's absmax overlaps the first one's error, and the order does not matter
+    bad = seg(g=A + off, e=Bp + off, c=Cp + off, a=Bp + 128)
+    assert cq(lib, [s0, bad]) == INV
+    assert cq(lib, [bad, s0]) == INV
+    # two segments writing the same error buffer
+    assert cq(lib, [s0, seg(g=A + off, c=Cp + off, a=Dp + off)]) == INV
+
+
 def pl(c=Cp, a=Dp):
     return loco.Payload(c, a)
 

@@ -292,3 +292,29 @@ def test_cq_teacher_forced(gpu_lib, ed):
             e_ora[::7] = np.float32(1e-4)
         for b, nm in ((g, "grad"), (e, "err"), (c, "codes"), (a, "absmax")):
             b.check(f"{tag} {nm}")
+
+
+def test_cq_segments_share_a_gradient(gpu_lib):
+    """Gradients are only read, so segments may overlap in them: two segments on the same
+    gradient tensor (and a third on an overlapping slice of it) each give the oracle's
+    result for their own range."""
+    n = 100_000 + 37
+    g = W.shard7b_grad(0, n=n, device="cuda", chain="shared")
+    views = [(0, n), (0, n), (4096, n)]  # the third starts at a block-aligned offset
+    outs = []
+    for lo, hi in views:
+        m = hi - lo
+        outs.append((torch.zeros(m, device="cuda"),
+                     torch.empty(gpu_lib.code_bytes(m, 4), dtype=torch.uint8, device="cuda"),
+                     torch.empty(gpu_lib.num_blocks(m, 256), device="cuda")))
+    say("cq segments sharing one gradient")
+    gpu_lib.loco_compensate_quantize([(g[lo:hi], e, c, a) for (lo, hi), (e, c, a) in zip(views, outs)],
+                                     bits=4, block=256, beta=0.9)
+    torch.cuda.synchronize()
+    for (lo, hi), (e, c, a) in zip(views, outs):
+        ref = oracle.compensate_quantize(bf16_bits(g[lo:hi]), np.zeros(hi - lo, np.float32), bits=4, block=256,
+                                         beta=0.9, grad_dtype="bf16")
+        t = f"segment on [{lo}, {hi})"
+        assert_bytes_equal(host(c), ref["codes"], f"{t} codes")
+        assert_bytes_equal(host(a).view(np.uint32), ref["absmax"].view(np.uint32), f"{t} absmax")
+        assert_f32_close(host(e), ref["e_new"], np.zeros(hi - lo), f"{t} error")
