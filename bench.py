@@ -202,6 +202,40 @@ def cpu_baseline_parallel(g_dev, payloads_dev, slab, per_worker=4):
             "sample": f"{elems:,} elements in {nslab} slabs of {slab:,}, {per_worker} per process, 2 steps each, "
                       f"{span:.1f} s from the processes' common start to the last one's end"}
 
+
+def _host_bf16(t):
+    """A bf16 device tensor as its uint16 bit patterns on the host."""
+    import numpy as np
+    import torch
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+
+def oracle_module():
+    import oracle
+    return oracle
+
+
+def _cq_job(gh, err, bits, block):
+    """One compensate-quantize step of the oracle on host gradient bits `gh` (bf16), from a
+    zero error of kind `err`."""
+    import numpy as np
+    zero = {"f32": np.zeros(gh.size, np.float32), "bf16": np.zeros(gh.size, np.uint16),
+            "i8": np.zeros(gh.size, np.int8)}[err]
+    return lambda: oracle_module().compensate_quantize(gh, zero, bits=bits, block=block, beta=BETA, grad_dtype="bf16",
+                                                       err_dtype=err, err_scale=2.0 ** 17 if err == "i8" else 0.0)
+
+def run_oracle_jobs(jobs, modes):
+    """Time each mode's oracle call (one call on a bounded sample of that mode's own
+    inputs, taken while they were on the device) and attach the GB/s of the sample's
+    algorithmic bytes to the mode: the oracle timed beside every kernel."""
+    for name, call, alg, sample in jobs:
+        t0 = time.perf_counter()
+        call()
+        dt = time.perf_counter() - t0
+        modes[name]["cpu_oracle"] = {"GBps": round(alg / dt / 1e9, 4), "seconds": round(dt, 3), "cores": 1,
+                                     "sample": sample}
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +253,7 @@ def main():
               "in memory); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import workloads as W
@@ -323,6 +358,8 @@ def main():
             kernels[k]["hbm_bytes_measured"] = v["hbm_bytes"]
 
     modes = {}
+    jobs = []  # (mode, oracle call on host copies of a sample of its inputs, sample's algorithmic bytes, what)
+    SAMPLE = 1 << 24
     if not args.no_modes:
         # 8-bit codes on the same shard and error-buffer layout
         codes8 = [torch.empty(part, dtype=torch.uint8, device=dev) for _ in range(PARTS)]
@@ -336,6 +373,8 @@ def main():
                                                       "GBps": round(b8 / ms / 1e6, 1),
                                                       "frac_hbm": round(b8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                                       "grad_GBps": round(n * 2 / ms / 1e6, 1)}
+        jobs.append(("compensate_quantize_8bit_7b_shard", _cq_job(_host_bf16(g[:SAMPLE]), "f32", 8, BLOCK),
+                     cq_bytes([SAMPLE], 2, 4, 8, BLOCK), f"the shard's first {SAMPLE:,} elements, one step"))
         del codes8, e8, segs8
         # the LLaMA-7B layer (7 bf16 gradients as 7 segments, fp32 error) and the MoE experts
         # (24 bf16 matrices with 30% zero rows, bf16 error): 4-bit, block 128
@@ -353,6 +392,10 @@ def main():
                             "error, 4-bit, block 128",
                 "avg_ms": round(ms, 4), **spread(), "alg_bytes": bx, "GBps": round(bx / ms / 1e6, 1),
                 "frac_hbm": round(bx / ms / 1e6 / HBM_PEAK_GBPS, 4), "grad_GBps": round(sum(xs) * 2 / ms / 1e6, 1)}
+            xe = "bf16" if edt == torch.bfloat16 else "f32"
+            jobs.append((f"compensate_quantize_4bit_{name}", _cq_job(_host_bf16(xg[0].reshape(-1)[:SAMPLE]), xe, 4, 128),
+                         cq_bytes([SAMPLE], 2, 2 if xe == "bf16" else 4, 4, 128),
+                         f"the first tensor's first {SAMPLE:,} elements, one step"))
             del xg, xsegs
         # the paper's 8-bit error (LoCo Eqn. (7), s_e = 2^17) with 4-bit codes, same shard
         ei8 = torch.zeros(n, dtype=torch.int8, device=dev)
@@ -366,6 +409,8 @@ def main():
                                                             "frac_hbm": round(bi8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                                             "grad_GBps": round(n * 2 / ms / 1e6, 1),
                                                             "err_scale": 2.0 ** 17}
+        jobs.append(("compensate_quantize_4bit_i8err_7b_shard", _cq_job(_host_bf16(g[:SAMPLE]), "i8", BITS, BLOCK),
+                     cq_bytes([SAMPLE], 2, 1, BITS, BLOCK), f"the shard's first {SAMPLE:,} elements, one step"))
         del ei8, segs_i8
         # the partition's payloads averaged straight into one LoCo-Adam step (Eqns. (8)-(9)):
         # fp32 weights and moments updated in place, plus the bf16 weight copy
@@ -383,6 +428,15 @@ def main():
                                                "avg_ms": round(ms, 4), **spread(), "alg_bytes": bda,
                                                "GBps": round(bda / ms / 1e6, 1),
                                                "frac_hbm": round(bda / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        ns = SAMPLE // 4
+        spl = [(c[:ns * BITS // 8].cpu().numpy(), a[:ns // BLOCK].cpu().numpy()) for c, a in payloads]
+        th_h = th[:ns].cpu().numpy()
+        jobs.append(("dequant_reduce_adam_8peers",
+                     lambda spl=spl, th_h=th_h, ns=ns: oracle_module().dequant_reduce_adam(
+                         spl, ns, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS, theta=th_h,
+                         m=np.zeros(ns, np.float32), v=np.zeros(ns, np.float32), lr=1e-4, beta1=0.1, beta2=0.01,
+                         delta=1e-8),
+                     dr_bytes(ns, PARTS, BITS, BLOCK, 0) + 26 * ns, f"the partition's first {ns:,} elements"))
         del th, m_, v_, tb
         # SparseLoCo-style mode on its own workload
         nt = W.SPARSE_N
@@ -401,6 +455,12 @@ def main():
                                          "avg_ms": round(ms, 4), **spread(), "alg_bytes": bt, "GBps": round(bt / ms / 1e6, 1),
                                          "frac_hbm": round(bt / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                          "grad_GBps": round(nt * 4 / ms / 1e6, 1)}
+        nts = 1024 * TK_CHUNK
+        gts = gt[:nts].cpu().numpy()
+        jobs.append(("sparseloco_topk_2bit",
+                     lambda gts=gts: oracle_module().topk_quantize(gts, np.zeros(gts.size, np.float32), chunk=TK_CHUNK,
+                                                                  k=TK_K, bits=2, decay=1.0),
+                     tk_bytes(nts, TK_CHUNK, TK_K, 2), f"the first 1,024 chunks ({nts:,} elements)"))
         del gt, et, idx, tcodes, tabs
         # SparseLoCo's sparse aggregation: 8 peers' Top-k payloads of the same shape into fp32 x 1/8
         spays = [W.random_sparse_payload(nt, TK_CHUNK, TK_K, 2, key=("bench", p), device=dev) for p in range(PARTS)]
@@ -414,6 +474,13 @@ def main():
                                                 "avg_ms": round(ms, 4), **spread(), "alg_bytes": bs,
                                                 "GBps": round(bs / ms / 1e6, 1),
                                                 "frac_hbm": round(bs / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        cb2, sch = (TK_K * 2 + 7) // 8, 8192
+        sps = [(ix[:sch * TK_K].cpu().numpy().view(np.uint16), c[:sch * cb2].cpu().numpy(), a[:sch].cpu().numpy())
+               for ix, c, a in spays]
+        jobs.append(("sparseloco_aggregate_8peers",
+                     lambda sps=sps: oracle_module().sparse_aggregate(sps, sch * TK_CHUNK, chunk=TK_CHUNK, k=TK_K,
+                                                                     bits=2, out_scale=1.0 / PARTS),
+                     sa_bytes(sch * TK_CHUNK, PARTS, TK_CHUNK, TK_K, 2, 4), f"the first {sch:,} chunks of the 8 payloads"))
         del spays, sout
 
     for k, v in measured.items():
@@ -431,6 +498,8 @@ def main():
         cpu = cpu_baseline(g, payloads, args.cpu_sample)
         log("bench: the same oracle fanned out over the host's cores")
         cpu["parallel"] = cpu_baseline_parallel(g, payloads, args.cpu_sample)
+        log("bench: the oracle on a sample of every mode's inputs")
+        run_oracle_jobs(jobs, modes)
 
     value = n * 2 / (ms_per_step / 1e3) / 1e9
     line = {
