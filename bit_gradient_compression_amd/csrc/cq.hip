@@ -9,12 +9,15 @@
 // and a step may store e' = 0 instead (the periodic reset of Eqn. (7)).
 //
 // Mapping: a wavefront owns a tile of sub-tiles of 512 elements (one sub-tile with a
-// float error, four with an 8-bit error, whose waves move fewer bytes); lane l owns 8
+// float error, two with an 8-bit error, whose waves move fewer bytes); lane l owns 8
 // consecutive elements of each sub-tile, so one bf16 gradient load, two fp32 error loads
 // (one 8-byte load of an 8-bit error) and one 32-bit code store per lane are coalesced.
 // A scale block of B elements is B/8 consecutive lanes; its absmax is reduced with DPP
 // row operations (and a permlane swap past 16 lanes).  Every load of a tile is issued
-// before any arithmetic.  The grid covers all wave tiles of all segments of the call:
+// before any arithmetic.  The 8-bit-error kernel is bound by VALU issue as much as by
+// HBM, so its per-element work is kept to a minimum: codes are packed from the float q
+// with v_cvt_pk_u8_f32, the int8 error is encoded by a magic-number add and v_perm, and
+// each block's two divisions are done once per wave, not once per lane.  The grid covers all wave tiles of all segments of the call:
 // each wave takes one tile and exits, so the waves in flight sweep the buffers in
 // address order (measured on MI355X, a persistent grid-stride loop over the same
 // traffic mix runs ~15% slower).
