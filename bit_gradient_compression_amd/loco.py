@@ -156,7 +156,20 @@ def num_blocks(n: int, block: int) -> int:
     return -(-n // block)
 
 
-def _segments(segments):
+# Sizes the C calls accept; for these, the binding checks that every tensor holds the bytes
+# the call will read or write (the C ABI sees only pointers and n).  Other values go to
+# the C call unchecked, which refuses them with its own status.
+_BITS = (2, 4, 8)
+_BLOCKS = (64, 128, 256, 512)
+_CHUNKS = (256, 512, 1024, 2048, 4096)
+
+
+def _need(t, nbytes: int, what: str) -> None:
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what} holds {t.numel() * t.element_size()} bytes; the call needs {nbytes}")
+
+
+def _segments(segments, bits=None, block=None, fixed=False):
     segs = list(segments)
     arr = (CqSegment * max(1, len(segs)))()
     gd = ed = None
@@ -165,15 +178,34 @@ def _segments(segments):
         ed = _dtype_code(e) if ed is None else ed
         if _dtype_code(g) != gd or _dtype_code(e) != ed:
             raise TypeError("all segments must share grad and err dtypes")
-        arr[i] = CqSegment(_ptr(g), _ptr(e), _ptr(c), _ptr(a), g.numel())
+        n = g.numel()
+        if e.numel() != n:
+            raise ValueError(f"segment {i}: err has {e.numel()} elements, grad {n}")
+        if n > 0 and bits in _BITS:
+            _need(c, code_bytes(n, bits), f"segment {i}: codes")
+            if not fixed and block in _BLOCKS:
+                _need(a, 4 * num_blocks(n, block), f"segment {i}: absmax")
+        arr[i] = CqSegment(_ptr(g), _ptr(e), _ptr(c), _ptr(a), n)
     return arr, len(segs), gd, ed
+
+
+def _payloads(peers, n, bits, block, fixed):
+    ps = list(peers)
+    arr = (Payload * max(1, len(ps)))()
+    for i, (c, a) in enumerate(ps):
+        if n > 0 and bits in _BITS:
+            _need(c, code_bytes(n, bits), f"peer {i}: codes")
+            if not fixed and block in _BLOCKS:
+                _need(a, 4 * num_blocks(n, block), f"peer {i}: absmax")
+        arr[i] = Payload(_ptr(c), _ptr(a))
+    return arr, ps
 
 
 def loco_compensate_quantize(segments, *, bits: int, block: int, beta: float, fixed_scale: float = 0.0,
                              stream=None, grad_dtype=None, err_dtype=None) -> None:
     """segments: iterable of (grad, err, codes, absmax) tensors; absmax may be None in
     fixed-scale mode.  n of a segment is grad.numel()."""
-    arr, nseg, gd, ed = _segments(segments)
+    arr, nseg, gd, ed = _segments(segments, bits, block, fixed_scale > 0)
     gd = gd if grad_dtype is None else grad_dtype
     ed = ed if err_dtype is None else err_dtype
     st = load().loco_compensate_quantize(arr, nseg, LOCO_F32 if gd is None else gd,
@@ -187,7 +219,7 @@ def loco_compensate_quantize_ex(segments, *, bits: int, block: int, beta: float,
                                 grad_dtype=None, err_dtype=None) -> None:
     """As loco_compensate_quantize; an int8 err tensor holds the 8-bit error of scale
     err_scale, and reset_error stores a zero error this step."""
-    arr, nseg, gd, ed = _segments(segments)
+    arr, nseg, gd, ed = _segments(segments, bits, block, fixed_scale > 0)
     gd = gd if grad_dtype is None else grad_dtype
     ed = ed if err_dtype is None else err_dtype
     opt = CqOptions(bits, block, beta, fixed_scale, err_scale, 1 if reset_error else 0)
@@ -200,10 +232,9 @@ def loco_compensate_quantize_ex(segments, *, bits: int, block: int, beta: float,
 def loco_dequant_reduce(peers, n: int, *, bits: int, block: int, out, out_scale: float,
                         fixed_scale: float = 0.0, stream=None) -> None:
     """peers: iterable of (codes, absmax) tensors (absmax None in fixed-scale mode)."""
-    ps = list(peers)
-    arr = (Payload * max(1, len(ps)))()
-    for i, (c, a) in enumerate(ps):
-        arr[i] = Payload(_ptr(c), _ptr(a))
+    arr, ps = _payloads(peers, n, bits, block, fixed_scale > 0)
+    if out is not None:
+        _need(out, n * out.element_size(), "out")
     st = load().loco_dequant_reduce(arr if ps else None, len(ps), n, bits, block, fixed_scale, out_scale,
                                     _ptr(out), _dtype_code(out), _stream(stream))
     _check("loco_dequant_reduce", st)
@@ -219,10 +250,10 @@ def loco_dequant_reduce_adam(peers, n: int, *, bits: int, block: int, out_scale:
             raise TypeError("param, m and v must be float32")
     if param_bf16 is not None and param_bf16.dtype != torch.bfloat16:
         raise TypeError("param_bf16 must be bfloat16")
-    ps = list(peers)
-    arr = (Payload * max(1, len(ps)))()
-    for i, (c, a) in enumerate(ps):
-        arr[i] = Payload(_ptr(c), _ptr(a))
+    arr, ps = _payloads(peers, n, bits, block, fixed_scale > 0)
+    for t, what in ((param, "param"), (m, "m"), (v, "v")):
+        _need(t, 4 * n, what)
+    _need(param_bf16, 2 * n, "param_bf16")
     hp = AdamParams(lr, beta1, beta2, delta)
     st = load().loco_dequant_reduce_adam(arr if ps else None, len(ps), n, bits, block, fixed_scale, out_scale,
                                          ctypes.byref(hp), _ptr(param), _ptr(m), _ptr(v), _ptr(param_bf16),
@@ -234,6 +265,14 @@ def loco_topk_quantize(grad, err, *, chunk: int, k: int, idx, codes, absmax, bit
                        ef_decay: float = 1.0, stream=None) -> None:
     if grad.dtype != torch.float32 or err.dtype != torch.float32:
         raise TypeError("grad and err must be float32")
+    n = grad.numel()
+    if err.numel() != n:
+        raise ValueError(f"err has {err.numel()} elements, grad {n}")
+    if n > 0 and chunk in _CHUNKS and 1 <= k <= chunk and bits in _BITS:
+        chunks = num_blocks(n, chunk)
+        _need(idx, 2 * chunks * k, "idx")
+        _need(codes, chunks * code_bytes(k, bits), "codes")
+        _need(absmax, 4 * chunks, "absmax")
     st = load().loco_topk_quantize(_ptr(grad), _ptr(err), grad.numel(), chunk, k, bits, ef_decay,
                                    _ptr(idx), _ptr(codes), _ptr(absmax), _stream(stream))
     _check("loco_topk_quantize", st)
@@ -245,8 +284,16 @@ def loco_sparse_aggregate(peers, n: int, *, chunk: int, k: int, out, out_scale: 
     loco_topk_quantize writes them."""
     ps = list(peers)
     arr = (SparsePayload * max(1, len(ps)))()
+    check = n > 0 and chunk in _CHUNKS and 1 <= k <= chunk and bits in _BITS
+    chunks = num_blocks(n, chunk) if check else 0
     for i, (ix, c, a) in enumerate(ps):
+        if check:
+            _need(ix, 2 * chunks * k, f"peer {i}: idx")
+            _need(c, chunks * code_bytes(k, bits), f"peer {i}: codes")
+            _need(a, 4 * chunks, f"peer {i}: absmax")
         arr[i] = SparsePayload(_ptr(ix), _ptr(c), _ptr(a))
+    if check and out is not None:
+        _need(out, n * out.element_size(), "out")
     st = load().loco_sparse_aggregate(arr if ps else None, len(ps), n, chunk, k, bits, out_scale, _ptr(out),
                                       _dtype_code(out), _stream(stream))
     _check("loco_sparse_aggregate", st)

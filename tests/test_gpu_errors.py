@@ -116,3 +116,40 @@ def test_binding_refuses_host_tensors(gpu_lib):
     e, c, a = cq_buffers(n)
     with pytest.raises(ValueError, match="device memory"):
         gpu_lib.loco_compensate_quantize([(g, e, c, a)], bits=4, block=256, beta=0.9)
+
+
+def test_binding_refuses_short_tensors(gpu_lib):
+    """The C ABI sees only pointers and n; the binding checks that every tensor holds the
+    bytes the call would touch, and refuses (ValueError) before any call."""
+    n = 10_000
+    g = W.shard7b_grad(0, n=n, device="cuda", chain="short")
+    e, c, a = cq_buffers(n)
+    before = snapshot(e, c, a)
+    with pytest.raises(ValueError, match="codes"):
+        gpu_lib.loco_compensate_quantize([(g, e, c[:-1], a)], bits=4, block=256, beta=0.9)
+    with pytest.raises(ValueError, match="absmax"):
+        gpu_lib.loco_compensate_quantize([(g, e, c, a[:-1])], bits=4, block=256, beta=0.9)
+    with pytest.raises(ValueError, match="elements"):
+        gpu_lib.loco_compensate_quantize([(g, e[:-1], c, a)], bits=4, block=256, beta=0.9)
+    unchanged(before, e, c, a)
+    pays = [tuple(x.cuda() for x in W.random_payload(n, 4, 256, key=("short", p))) for p in range(2)]
+    out = torch.zeros(n - 1, device="cuda")
+    with pytest.raises(ValueError, match="out"):
+        gpu_lib.loco_dequant_reduce(pays, n, bits=4, block=256, out=out, out_scale=0.5)
+    with pytest.raises(ValueError, match="peer 1: codes"):
+        gpu_lib.loco_dequant_reduce([pays[0], (pays[1][0][:-1], pays[1][1])], n, bits=4, block=256,
+                                    out=torch.zeros(n, device="cuda"), out_scale=0.5)
+    with pytest.raises(ValueError, match="v holds"):
+        gpu_lib.loco_dequant_reduce_adam(pays, n, bits=4, block=256, out_scale=0.5, param=torch.zeros(n, device="cuda"),
+                                         m=torch.zeros(n, device="cuda"), v=torch.zeros(n - 4, device="cuda"),
+                                         lr=1e-3, beta1=0.1, beta2=0.01, delta=1e-8)
+    nt, chunk, k = 2 * 4096 + 5, 4096, 82
+    gt = torch.zeros(nt, device="cuda")
+    with pytest.raises(ValueError, match="idx"):
+        gpu_lib.loco_topk_quantize(gt, torch.zeros(nt, device="cuda"), chunk=chunk, k=k,
+                                   idx=torch.zeros(3 * k - 1, dtype=torch.int16, device="cuda"),
+                                   codes=torch.zeros(3 * 21, dtype=torch.uint8, device="cuda"),
+                                   absmax=torch.zeros(3, device="cuda"))
+    sp = [tuple(x.cuda() for x in W.random_sparse_payload(nt, chunk, k, 2, key=("short", 0)))]
+    with pytest.raises(ValueError, match="out"):
+        gpu_lib.loco_sparse_aggregate(sp, nt, chunk=chunk, k=k, out=torch.zeros(nt - 1, device="cuda"), out_scale=1.0)
