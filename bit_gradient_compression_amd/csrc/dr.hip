@@ -51,13 +51,13 @@ __device__ __forceinline__ void acc_byte(float& a, uint32_t x, float step, float
 // converts, and fl(q*step) is formed as fma(q + 2^(b-1), step, -2^(b-1)*step): the fma's
 // exact value is q*step, rounded once, so the result is bit-identical to rounding q*step
 // (2^(b-1)*step is exact).  2-bit codes use a sign-extending bit-field extract.
+// off is -2^(b-1)*step, computed by the caller (once per scale, not per 8 codes).
 template <int BITS>
-__device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float step) {
+__device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float step, float off) {
     if constexpr (BITS == 4) {
         const uint32_t x = w.x ^ 0x88888888u;
         const uint32_t lo = x & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
         const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-        const float off = -8.0f * step;
         acc_byte<0>(acc[0], lo, step, off);
         acc_byte<0>(acc[1], hi, step, off);
         acc_byte<1>(acc[2], lo, step, off);
@@ -68,7 +68,6 @@ __device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float
         acc_byte<3>(acc[7], hi, step, off);
     } else if constexpr (BITS == 8) {
         const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
-        const float off = -128.0f * step;
         acc_byte<0>(acc[0], x0, step, off);
         acc_byte<1>(acc[1], x0, step, off);
         acc_byte<2>(acc[2], x0, step, off);
@@ -201,16 +200,32 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                     }
                     stp = am / (float)QMAX;  // 0 for an all-zero block
                 }
+                // the decoder's offset -2^(b-1)*step (exact), formed once per scale
+                const float offp = -(float)(1 << (BITS - 1)) * stp;
                 for (int q0 = 0; q0 < ng; q0 += kDrPeerBatch) {
                     if (q0 > 0) load_batch(q0);
+                    // byte address (ds_bpermute) of the lane holding peer q0's scale of this
+                    // lane's block in sub-tile u; peer q0 + b is b*BPT lanes further, an
+                    // immediate offset
+                    int src[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) src[u] = (q0 * BPT + myblk[u]) * 4;
                     // accumulate in peer order
 #pragma unroll
                     for (int b = 0; b < kDrPeerBatch; ++b) {
                         if (q0 + b < ng) {
 #pragma unroll
                             for (int u = 0; u < U; ++u) {
-                                const float step = FIXED ? stp : __shfl(stp, (q0 + b) * BPT + myblk[u], 64);
-                                accumulate8<BITS>(acc[u], w[b][u], step);
+                                float step = stp, off = offp;
+                                if constexpr (!FIXED) {
+                                    const int a = src[u] + b * BPT * 4;
+                                    step = __builtin_bit_cast(
+                                        float, __builtin_amdgcn_ds_bpermute(a, __builtin_bit_cast(int, stp)));
+                                    if constexpr (BITS != 2)
+                                        off = __builtin_bit_cast(
+                                            float, __builtin_amdgcn_ds_bpermute(a, __builtin_bit_cast(int, offp)));
+                                }
+                                accumulate8<BITS>(acc[u], w[b][u], step, off);
                             }
                         }
                     }
