@@ -10,7 +10,10 @@ step to step.  Compensate-quantize on the LLaMA-7B layer and MoE-expert workload
 SparseLoCo-style Top-k mode (2^28 fp32, chunk 4096, k = 82, 2-bit),
 its sparse aggregation of 8 peers' payloads, the 8-bit-code variant, the 8-bit-error
 variant (LoCo Eqn. (7)) and dequant-reduce fused with the LoCo-Adam step (Eqn. (9)) are
-timed in the same run and reported under "modes".
+timed in the same run and reported under "modes".  So is the tiny case (1,048,576 fp32,
+compensate-quantize then dequant-reduce of 4 peers), which fits in the Infinity Cache and
+is bound by launch latency: its time per step is reported eagerly and as replays of a HIP
+graph, with no roofline claim.
 
 Each mode is timed back to back and again with a 1 GiB read before each launch (which
 keeps its inputs out of the Infinity Cache and keeps other launches' dirty lines out of
@@ -40,6 +43,7 @@ HBM_PEAK_GBPS = 8000.0
 PARTS = 8
 BITS, BLOCK, BETA = 4, 256, 0.9
 TK_CHUNK, TK_K = 4096, 82
+TINY_N, TINY_BLOCK, TINY_PEERS = 1 << 20, 128, 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard.json")
 CSRC = os.path.join(ROOT, "bit_gradient_compression_amd", "csrc")
 KERNEL_FILES = {"compensate_quantize_4bit": ["cq.hip"], "dequant_reduce_8peers": ["dr.hip"],
@@ -483,6 +487,64 @@ def main():
                      sa_bytes(sch * TK_CHUNK, PARTS, TK_CHUNK, TK_K, 2, 4), f"the first {sch:,} chunks of the 8 payloads"))
         del spays, sout
 
+        # the tiny case: 1,048,576 fp32 elements, one compensate-quantize (4-bit, block 128)
+        # and the dequant-reduce of 4 peers into fp32 x 1/4 per step.  Its 19.6 MB sit in the
+        # Infinity Cache and launch latency bounds it, so it gets no roofline claim: the time
+        # per step over 200 back-to-back steps, launched eagerly and as replays of a HIP
+        # graph that holds 20 steps.
+        tn = TINY_N
+        tg = W.tiny_grad(0, n=tn).to(dev)
+        te = torch.zeros(tn, device=dev)
+        tcd = torch.empty(loco.code_bytes(tn, BITS), dtype=torch.uint8, device=dev)
+        tam = torch.empty(loco.num_blocks(tn, TINY_BLOCK), device=dev)
+        tpays = []
+        for pgr in W.tiny_peer_grads(TINY_PEERS, n=tn):
+            tp = (torch.empty_like(tcd), torch.empty_like(tam))
+            loco.loco_compensate_quantize([(pgr.to(dev), torch.zeros(tn, device=dev), *tp)], bits=BITS,
+                                          block=TINY_BLOCK, beta=BETA)
+            tpays.append(tp)
+        tout = torch.empty(tn, device=dev)
+
+        def tiny_step():  # on the current stream
+            loco.loco_compensate_quantize([(tg, te, tcd, tam)], bits=BITS, block=TINY_BLOCK, beta=BETA)
+            loco.loco_dequant_reduce(tpays, tn, bits=BITS, block=TINY_BLOCK, out=tout, out_scale=1.0 / TINY_PEERS)
+
+        def per_step_us(launch, steps_per_launch, launches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    launch()
+                a.record(stream)
+                for _ in range(launches):
+                    launch()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / (steps_per_launch * launches)
+
+        torch.cuda.synchronize()
+        eager_us = per_step_us(tiny_step, 1, 200)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(20):
+                tiny_step()
+        torch.cuda.synchronize()
+        graph_us = per_step_us(graph.replay, 20, 10)
+        bt = cq_bytes([tn], 4, 4, BITS, TINY_BLOCK) + dr_bytes(tn, TINY_PEERS, BITS, TINY_BLOCK, 4)
+        modes["tiny_1m_cq_dr_4peers"] = {
+            "workload": f"{tn:,} fp32 N(0,1e-3), fp32 error, 4-bit block {TINY_BLOCK}; then dequant-reduce of "
+                        f"{TINY_PEERS} peer payloads into fp32 x 1/{TINY_PEERS}",
+            "cache_resident": True, "us_per_step_eager": round(eager_us, 2), "us_per_step_graph": round(graph_us, 2),
+            "alg_bytes": bt, "GBps": round(bt / graph_us / 1e3, 1),
+            "note": "launch-latency bound, inside the Infinity Cache: no roofline claim; GBps from the graph replays"}
+        tgh, tph = tg.cpu().numpy(), [(c.cpu().numpy(), a.cpu().numpy()) for c, a in tpays]
+        jobs.append(("tiny_1m_cq_dr_4peers",
+                     lambda: (oracle_module().compensate_quantize(tgh, np.zeros(tn, np.float32), bits=BITS,
+                                                                  block=TINY_BLOCK, beta=BETA),
+                              oracle_module().dequant_reduce(tph, tn, bits=BITS, block=TINY_BLOCK,
+                                                             out_scale=1.0 / TINY_PEERS)),
+                     bt, f"the whole step ({tn:,} elements)"))
+        del graph, tg, te, tcd, tam, tpays, tout
+
     for k, v in measured.items():
         if k in modes:
             modes[k]["hbm_bytes_measured"] = v["hbm_bytes"]
@@ -490,7 +552,8 @@ def main():
 
     for table in (kernels, modes):
         for v in table.values():
-            v["frac_copy"] = round(v["GBps"] / copy_gbps, 4)
+            if not v.get("cache_resident"):
+                v["frac_copy"] = round(v["GBps"] / copy_gbps, 4)
 
     cpu = None
     if args.cpu_sample > 0:

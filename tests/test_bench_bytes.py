@@ -45,6 +45,17 @@ def test_dequant_reduce_bytes():
     assert oracle.dra_algorithmic_bytes(part, 8, 4, 256, param_bf16=True) == dra
 
 
+def test_tiny_bytes():
+    # 1,048,576 fp32 gradient and error, 4-bit codes, block 128: 12.5 bytes per element + 4
+    # per block; dequant-reduce of 4 peers into fp32
+    n = bench.TINY_N
+    assert n == W.TINY_N == 1 << 20
+    assert bench.cq_bytes([n], 4, 4, 4, 128) == n * 25 // 2 + 4 * (n // 128) == 13_139_968
+    assert bench.dr_bytes(n, 4, 4, 128, 4) == 4 * (n // 2 + 4 * (n // 128)) + 4 * n == 6_422_528
+    assert oracle.cq_algorithmic_bytes(n, 4, 4, 4, 128) == 13_139_968
+    assert oracle.dr_algorithmic_bytes(n, 4, 4, 128, 4) == 6_422_528
+
+
 def test_sparseloco_bytes():
     n, C, k = 1 << 28, 4096, 82
     chunks = n // C
