@@ -18,7 +18,9 @@
 // dense chunk is then written once, each thread storing whole runs of up to 8 outputs.
 // Two kernels: a streaming one (k <= NT, at most kSaPeerBatch peers: the usual case), a
 // persistent grid of a few workgroups per compute unit that loads each chunk's payload
-// while it processes the previous chunk; and a general one, one workgroup per chunk.
+// while it processes the previous chunk, and first reads the payloads of many chunks in a
+// read-only pass so that its output writes meet no DRAM reads; and a general one, one
+// workgroup per chunk.
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"

@@ -153,3 +153,15 @@ def test_binding_refuses_short_tensors(gpu_lib):
     sp = [tuple(x.cuda() for x in W.random_sparse_payload(nt, chunk, k, 2, key=("short", 0)))]
     with pytest.raises(ValueError, match="out"):
         gpu_lib.loco_sparse_aggregate(sp, nt, chunk=chunk, k=k, out=torch.zeros(nt - 1, device="cuda"), out_scale=1.0)
+
+
+def test_binding_missing_buffers(gpu_lib):
+    """A missing output or payload buffer (None) reaches the C call as a null pointer, which
+    refuses it (LOCO_ERR_INVALID) before any launch."""
+    n = 4096
+    pays = [tuple(x.cuda() for x in W.random_payload(n, 4, 256, key=("none", p))) for p in range(2)]
+    refused(INV, gpu_lib.loco_dequant_reduce, pays, n, bits=4, block=256, out=None, out_scale=0.5)
+    refused(INV, gpu_lib.loco_dequant_reduce, [pays[0], (pays[1][0], None)], n, bits=4, block=256,
+            out=torch.zeros(n, device="cuda"), out_scale=0.5)
+    sp = [tuple(x.cuda() for x in W.random_sparse_payload(n, 4096, 82, 2, key=("none", 0)))]
+    refused(INV, gpu_lib.loco_sparse_aggregate, sp, n, chunk=4096, k=82, out=None, out_scale=1.0)
