@@ -22,9 +22,11 @@
  * Conventions shared by every entry point
  *   - Device pointers are caller-owned device memory (e.g. PyTorch tensors) and must
  *     be 16-byte aligned; host arrays (segs, peers) are read during the call only.
- *   - The library allocates nothing and keeps no state between calls.  Every call is
- *     asynchronous on `stream` (a hipStream_t; NULL is the default stream); buffers
- *     must stay alive until the stream has consumed them.
+ *   - The library allocates nothing and keeps no state between calls, apart from the
+ *     compute-unit count of each device, read once and cached.  Every call is
+ *     asynchronous on `stream` (a hipStream_t; NULL is the default stream) and runs on
+ *     the calling thread's current device; buffers must stay alive until the stream has
+ *     consumed them.
  *   - Arguments are validated on the host before anything is launched: an error
  *     status means nothing was launched and nothing was written.  Device faults
  *     surface at the caller's next synchronisation, as for any HIP call.
@@ -168,6 +170,7 @@ typedef struct {
  *   fixed_scale 0, or the s the payloads were made with
  *   out_scale  finite
  *   out        device, n elements of out_dtype (written); must not overlap a payload
+ *   out_dtype  LOCO_F32 or LOCO_BF16
  */
 int loco_dequant_reduce(const loco_payload_t* peers, int npeers, int64_t n,
                         int bits, int block, float fixed_scale, float out_scale,
@@ -260,6 +263,7 @@ typedef struct {
  *   chunk      256, 512, 1024, 2048 or 4096;  1 <= k <= chunk;  bits 2, 4 or 8
  *   out_scale  finite
  *   out        device, n elements of out_dtype (written); must not overlap a payload
+ *   out_dtype  LOCO_F32 or LOCO_BF16
  * where chunks = ceil(n / chunk).
  */
 int loco_sparse_aggregate(const loco_sparse_payload_t* peers, int npeers, int64_t n,
