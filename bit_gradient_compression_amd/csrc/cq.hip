@@ -17,10 +17,11 @@
 // before any arithmetic.  The 8-bit-error kernel is bound by VALU issue as much as by
 // HBM, so its per-element work is kept to a minimum: codes are packed from the float q
 // with v_cvt_pk_u8_f32, the int8 error is encoded by a magic-number add and v_perm, and
-// each block's two divisions are done once per wave, not once per lane.  The grid covers all wave tiles of all segments of the call:
-// each wave takes one tile and exits, so the waves in flight sweep the buffers in
-// address order (measured on MI355X, a persistent grid-stride loop over the same
-// traffic mix runs ~15% slower).
+// a wave issues the two divisions of its blocks once for both sub-tiles (each lane
+// divides for one block; the results are shuffled to the block's lanes).
+// The grid covers all wave tiles of all segments of the call: each wave takes one tile
+// and exits, so the waves in flight sweep the buffers in address order (measured on
+// MI355X, a persistent grid-stride loop over the same traffic mix runs ~15% slower).
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"

@@ -318,13 +318,12 @@ __global__ __launch_bounds__(NT) void sa_stream_kernel(SaParams p) {
     }
 }
 
-// Launch shape per output type, measured on MI355X for 8 peers of 2^28 in chunks of 4096
-// (payloads out of the Infinity Cache / still in it): 128 threads per chunk; fp32 out with
-// 3 workgroups per compute unit 0.254 / 0.207 ms, against 0.28 / 0.21 with 6 and 0.28 /
-// 0.21 with 2; bf16 out with 8, 0.168 / 0.107 ms.  The output is ~92% of the bytes, and
-// dense writes run best with few waves in flight.  Loading two chunks ahead instead of
-// one changed nothing: the time goes to the writes and their mix with the payload reads,
-// not to waiting for the payloads.
+// Launch shape per output type, measured on MI355X for 8 peers of 2^28 in chunks of 4096,
+// with the read passes (cache-cold / back to back): 128 threads per chunk; fp32 out with
+// 3 workgroups per compute unit 0.211 / 0.206 ms, against 0.331 / 0.330 with 1, 0.258 /
+// 0.245 with 2, 0.241 / 0.229 with 4 and 0.241 / 0.221 with 6; bf16 out with 8, 0.130 /
+// 0.117 ms.  The output is ~92% of the bytes, and dense writes run best with few waves in
+// flight, but fewer than 3 workgroups leave the payload loads' latency exposed.
 template <int C, int BITS>
 void pick_out(bool out_bf16, bool stream, const void*& k) {
     if (stream)

@@ -294,3 +294,59 @@ def test_dra_checks(lib, kwargs, want):
 def test_dra_noop(lib):
     assert dra(lib, [pl()], n=0) == OK
     assert dra(lib, [pl()], n=0, param=0) == OK
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "loco.h"
+
+/* Only calls that fail validation or have nothing to do: nothing is launched. */
+int main(void) {
+    int bad = 0;
+    loco_cq_segment_t seg;
+    loco_payload_t pay;
+    loco_sparse_payload_t sp;
+    loco_cq_options_t opt;
+    loco_adam_t adam = {1e-3f, 0.1f, 0.01f, 1e-8f};
+    memset(&seg, 0, sizeof seg);
+    memset(&pay, 0, sizeof pay);
+    memset(&sp, 0, sizeof sp);
+    memset(&opt, 0, sizeof opt);
+    opt.bits = 4; opt.block = 256; opt.beta = 0.9f;
+    if (loco_version() <= 0) bad |= 1;
+    if (strlen(loco_status_string(LOCO_ERR_ALIGN)) == 0) bad |= 2;
+    /* a null segment array with one segment, and a zero-length segment */
+    if (loco_compensate_quantize(NULL, 1, LOCO_BF16, LOCO_F32, 4, 256, 0.9f, 0.0f, NULL) != LOCO_ERR_INVALID) bad |= 4;
+    if (loco_compensate_quantize(&seg, 1, LOCO_BF16, LOCO_F32, 4, 256, 0.9f, 0.0f, NULL) != LOCO_OK) bad |= 8;
+    if (loco_compensate_quantize_ex(&seg, 1, LOCO_BF16, LOCO_F32, NULL, NULL) != LOCO_ERR_INVALID) bad |= 16;
+    if (loco_compensate_quantize_ex(&seg, 1, LOCO_BF16, LOCO_F32, &opt, NULL) != LOCO_OK) bad |= 32;
+    if (loco_dequant_reduce(&pay, 0, 16, 4, 256, 0.0f, 1.0f, NULL, LOCO_F32, NULL) != LOCO_ERR_INVALID) bad |= 64;
+    if (loco_dequant_reduce_adam(&pay, 1, 16, 4, 256, 0.0f, 1.0f, &adam, NULL, NULL, NULL, NULL, NULL)
+        != LOCO_ERR_INVALID) bad |= 128;
+    if (loco_topk_quantize(NULL, NULL, 0, 4096, 82, 2, 1.0f, NULL, NULL, NULL, NULL) != LOCO_OK) bad |= 256;
+    if (loco_sparse_aggregate(&sp, 1, 16, 4096, 82, 3, 1.0f, NULL, LOCO_F32, NULL) != LOCO_ERR_UNSUPPORTED)
+        bad |= 512;
+    printf("bad=%d\n", bad);
+    return bad != 0;
+}
+"""
+
+
+@pytest.mark.parametrize("lang", ["c99", "c++17"])
+def test_header_compiles_and_links_from_c(lib, tmp_path, lang):
+    """include/loco.h is plain C (and C++ through its extern "C" block): a program built
+    with warnings as errors links against the library and gets the documented statuses
+    from calls that only validate."""
+    cxx = lang.startswith("c++")
+    src = tmp_path / ("prog.cpp" if cxx else "prog.c")
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "prog"
+    libdir = os.path.dirname(B.LIB_PATH)
+    cmd = ["g++" if cxx else "gcc", f"-std={lang}", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe), f"-L{libdir}", "-lloco",
+           f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "bad=0" in r.stdout, r.stdout + r.stderr
