@@ -48,6 +48,13 @@ Readings where the pages are silent (each is also listed in the design notes):
   m follows it by analogy), no bias correction and no weight decay (the page names
   neither), theta' = theta - lr * (m' * u) with u = 1 / sqrt(v' + delta).
 
+Parity unpinned: where the pages leave the form open, only the readings above
+decide it: the form of the moving average (Eqn. (5)), the 2-bit codebook, the
+SparseLoCo error-feedback decay, the form of the sparse aggregation, and the m
+recursion and update order of the Adam-family step (Eqn. (9)).  The tests pin
+every function to closed forms, bounds and worked examples under these readings;
+the pages cannot choose between the readings.
+
 The functions are generic over the float type of their inputs: called with
 float32 arrays they are the parity oracle; called with float64 arrays they are
 the real-arithmetic twin used by the telescoping check.
