@@ -27,9 +27,13 @@
  *     asynchronous on `stream` (a hipStream_t; NULL is the default stream) and runs on
  *     the calling thread's current device; buffers must stay alive until the stream has
  *     consumed them.
- *   - Arguments are validated on the host before anything is launched: an error
- *     status means nothing was launched and nothing was written.  Device faults
- *     surface at the caller's next synchronisation, as for any HIP call.
+ *   - Arguments are validated on the host before anything is launched: a validation
+ *     status (LOCO_ERR_INVALID, LOCO_ERR_ALIGN, LOCO_ERR_UNSUPPORTED) means nothing was
+ *     launched and nothing was written.  LOCO_ERR_HIP means a kernel launch failed; a
+ *     call that takes several launches (more than 32 segments, a short last Top-k
+ *     chunk, or more chunks than one grid holds) may have enqueued the launches before
+ *     it.  Device faults surface at the caller's next synchronisation, as for any HIP
+ *     call.
  *   - Arithmetic: IEEE binary32, round to nearest even, no fused multiply-add, in
  *     the order stated below; bf16 stores round to nearest even.
  *   - Stateless and reentrant across host threads and streams.
@@ -47,7 +51,7 @@ extern "C" {
  * loco_compensate_quantize_ex: the paper's 8-bit error codes of a fixed scale s_e. */
 typedef enum { LOCO_F32 = 0, LOCO_BF16 = 1, LOCO_I8 = 2 } loco_dtype_t;
 
-/* Status codes: 0 ok, < 0 error (nothing launched). */
+/* Status codes: 0 ok, < 0 error (nothing launched, except as LOCO_ERR_HIP below). */
 #define LOCO_OK 0
 #define LOCO_ERR_INVALID (-1)     /* bad size, bits, block, k, chunk, beta, scale, dtype,
                                      peer count < 1, null pointer, or overlapping buffers */
