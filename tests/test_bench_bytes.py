@@ -66,3 +66,26 @@ def test_sparseloco_bytes():
     # sparse aggregation: 8 peers' payloads read, fp32 out written
     assert bench.sa_bytes(n, 8, C, k, 2, 4) == 8 * chunks * (164 + 21 + 4) + 4 * n == 1_172_832_256
     assert oracle.sa_algorithmic_bytes(n, 8, C, k, 2, 4) == 1_172_832_256
+
+
+def test_traffic_summary_dropped_when_kernel_changes(tmp_path, monkeypatch):
+    """bench.py reports a kernel's measured HBM bytes only while the kernel's sources hash
+    to what the counter summary recorded; a summary taken before a change gives null."""
+    import json
+    kernels = {k: {"hbm_bytes": 1000 + i, "source_hash": bench.kernel_source_hash(k)}
+               for i, k in enumerate(sorted(bench.KERNEL_FILES))}
+    stale = "compensate_quantize_4bit"
+    kernels[stale]["source_hash"] = "0" * 16
+    kernels["not_a_kernel"] = {"hbm_bytes": 1, "source_hash": "x"}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps({"kernels": kernels}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    got = bench.load_traffic()
+    assert set(got) == set(bench.KERNEL_FILES) - {stale}
+    # every kernel's hash covers source files that exist, plus the shared headers
+    import os
+    for k, files in bench.KERNEL_FILES.items():
+        assert files and all(os.path.isfile(os.path.join(bench.CSRC, x)) for x in files + bench.COMMON_FILES)
+        assert len(bench.kernel_source_hash(k)) == 16
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
+    assert bench.load_traffic() == {}
