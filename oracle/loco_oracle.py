@@ -33,7 +33,9 @@ extracted text, so each step below is rebuilt from the prose around the equation
 Readings where the pages are silent (each is also listed in the design notes):
 * per-block absmax scale: the stored scale is the block's max |h| (exact); the
   dequantisation step is fl(absmax / qmax) and quantisation multiplies by the
-  explicit reciprocal fl(1 / step); an all-zero block has step = inv = 0.
+  explicit reciprocal fl(1 / step).  Where that reciprocal is not finite (an
+  all-zero block, or a block whose absmax is below ~qmax * 2^-128, where 1/step
+  overflows fp32) inv = 0: the block is sent as zero codes and stays in the error.
 * "nearest integer" ties go to even (PyTorch's default quantiser does this).
 * the moving average is e' = beta * e + (1 - beta) * r with r = h - d.
 * every floating-point value is one IEEE binary32 operation (round to nearest
@@ -65,7 +67,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_rne", "bf16_to_f32", "widen", "qmax_of",
+    "bf16_rne", "bf16_to_f32", "widen", "qmax_of", "finite_reciprocal",
     "compensate", "absmax_quantize", "fixed_scale_quantize", "dequantize",
     "error_update", "error_decompress", "error_compress", "pack_codes", "unpack_codes",
     "compensate_quantize",
@@ -136,21 +138,35 @@ def absmax_quantize(h: np.ndarray, bits: int, block: int):
     """Eqn. (1) with a per-block absmax scale instead of the paper's global s.
 
     Blocks tile h from element 0; the last block may be partial (its padding is
-    zero, which cannot change a max of absolute values).  Returns
+    zero, which cannot change a max of absolute values).  step = fl(absmax / qmax),
+    inv = fl(1 / step), q = clamp(rint(fl(h * inv))).  A block whose reciprocal is
+    not finite (an all-zero block, or one so small that 1/step overflows) gets
+    inv = 0: its codes are 0 and its values stay whole in the error.  Returns
     (q int64[n], absmax[nb], step[nb]) in h's float type.
     """
     ft = h.dtype.type
     qmax = qmax_of(bits)
     hb, nb = _blocks(h, block)
     absmax = np.max(np.abs(hb), axis=1)
-    nz = absmax != 0
-    step = np.zeros(nb, dtype=h.dtype)
-    np.divide(absmax, ft(qmax), out=step, where=nz)
-    inv = np.zeros(nb, dtype=h.dtype)
-    np.divide(ft(1), step, out=inv, where=nz)
+    step = absmax / ft(qmax)
+    inv = finite_reciprocal(step)
     scaled = hb * inv[:, None]
     q = np.clip(np.rint(scaled), -(qmax + 1), qmax).astype(np.int64)
     return q.reshape(-1)[: h.size], absmax, step
+
+
+def finite_reciprocal(step: np.ndarray) -> np.ndarray:
+    """inv = fl(1 / step), or 0 where that is not finite.
+
+    step >= 0.  The reciprocal is +inf for step = 0 (an all-zero block) and for a step
+    below about 2^-128 in fp32, where 1/step exceeds the largest finite float.  Such a
+    block cannot be scaled into the code range, so it is sent as zero codes (inv = 0
+    makes every q = 0) and the error feedback keeps its values.
+    """
+    step = np.asarray(step)
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = step.dtype.type(1) / step
+    return np.where(np.isfinite(inv), inv, step.dtype.type(0)).astype(step.dtype)
 
 
 def fixed_scale_quantize(h: np.ndarray, bits: int, s: float):
@@ -386,7 +402,8 @@ def topk_quantize(g, e, *, chunk, k, bits=2, decay=1.0, ftype=np.float32):
     Per chunk of `chunk` elements (the last may be short; it keeps min(k, len)):
       h = g + decay * e                 error feedback
       select the k largest |h| (bit pattern of |h|; ties to the lower index)
-      absmax over the kept values; step = absmax / qmax; inv = 1 / step (0 if 0)
+      absmax over the kept values; step = absmax / qmax; inv = 1 / step, or 0
+      where that is not finite (absmax 0, or below ~2^-128 * qmax)
       q = clamp(rint(h * inv)) on the kept values
       e' = h - q * step on the kept values, e' = h elsewhere
     Returns dict(idx uint16[chunks*k] (unused slots 0xFFFF), codes
@@ -411,11 +428,8 @@ def topk_quantize(g, e, *, chunk, k, bits=2, decay=1.0, ftype=np.float32):
         sel = topk_order_select(key, keff)
         vals = hc[sel]
         absmax = np.max(np.abs(vals))
-        step = ftype(0)
-        inv = ftype(0)
-        if absmax != 0:
-            step = absmax / ftype(qmax)
-            inv = ftype(1) / step
+        step = absmax / ftype(qmax)
+        inv = finite_reciprocal(np.array([step], dtype=ftype))[0]
         q = np.clip(np.rint(vals * inv), -(qmax + 1), qmax).astype(np.int64)
         d = q.astype(ftype) * step
         e_new[lo + sel] = vals - d

@@ -104,3 +104,20 @@ def adam_case():
         v = rest.split()
         d[k] = float(v[0]) if len(v) == 1 and k in ("lr", "beta1", "beta2", "delta") else np.array(v, np.float32)
     return d
+
+
+def dra_case():
+    d = {"peers": []}
+    for ln in _lines("dra_worked.txt"):
+        k, rest = ln.split(None, 1)
+        if k == "peer":
+            hx, am = rest.split("|")
+            d["peers"].append((np.frombuffer(bytes.fromhex(hx.replace(" ", "")), np.uint8).copy(),
+                               np.array(am.split(), np.float32)))
+        elif k in ("bits", "block", "n"):
+            d[k] = int(rest)
+        elif k in ("out_scale", "lr", "beta1", "beta2", "delta"):
+            d[k] = float(rest)
+        else:
+            d[k] = np.array(rest.split(), np.float32)
+    return d

@@ -658,6 +658,120 @@ def pin_adam_limits(O):
     assert np.array_equal(m3, (F32(1) - F32(0.1)) * m) and np.array_equal(v3, (F32(1) - F32(0.01)) * v)
 
 
+def pin_dra_worked(O):
+    """Eqn. (8) feeding Eqn. (9) on a hand-worked case whose average is exact in fp32 but
+    not in bf16: the gradient of the step is the fp32 average (never rounded to bf16), the
+    step uses the average (out_scale applied before it), and the weight copy is rounded to
+    nearest even."""
+    c = golden_io.dra_case()
+    r = O.dequant_reduce_adam(c["peers"], c["n"], bits=c["bits"], block=c["block"], out_scale=c["out_scale"],
+                              theta=c["theta"], m=c["m"], v=c["v"], lr=c["lr"], beta1=c["beta1"],
+                              beta2=c["beta2"], delta=c["delta"])
+    for key, want in (("g", "g"), ("m", "m_new"), ("v", "v_new"), ("theta", "theta_new")):
+        assert np.array_equal(np.asarray(r[key], F32).view(np.uint32), c[want].view(np.uint32)), (key, r[key], c[want])
+    tb = np.asarray(r["theta_bf16"], np.uint16).astype(np.uint32) << np.uint32(16)
+    assert np.array_equal(tb.view(np.float32), c["theta_bf16"]), (tb.view(np.float32), c["theta_bf16"])
+
+
+# -- blocks too small for a finite reciprocal (absmax below ~qmax * 2^-128) ------------------------
+
+# IEEE binary32 overflow under round to nearest: a real result of magnitude at least
+# 2^128 - 2^103 (the largest finite value plus half its ulp) rounds to infinity.
+_F32_OVERFLOW = 2.0 ** 128 - 2.0 ** 103
+
+
+def _tiny_blocks(rng, block, qmax, nblocks):
+    """Blocks of subnormal / near-subnormal values: half with absmax far below the
+    reciprocal's overflow (1/(absmax/qmax) >= 4 * 2^128), half with a subnormal step
+    in [2^-127, 1.7 * 2^-127) whose reciprocal is finite; some exact zeros inside every
+    block, one all-zero block."""
+    out, kind = [], []
+    for b in range(nblocks):
+        if b == nblocks - 1:
+            out.append(np.zeros(block, F32))
+            kind.append("zero")
+            continue
+        over = b % 2 == 0
+        # target absmax: qmax * 2^-131 .. qmax * 2^-130 (overflowing) or
+        # qmax * 2^-127 .. qmax * 1.7 * 2^-127 (a subnormal step, finite reciprocal)
+        if over:
+            hi = qmax * 2.0 ** -130 * (0.5 + 0.5 * rng.random())
+        else:
+            hi = qmax * 2.0 ** -127 * (1.0 + 0.7 * rng.random())
+        x = (rng.random(block) * 2 - 1) * hi
+        x[rng.random(block) < 0.2] = 0.0
+        x[int(rng.integers(0, block))] = hi if rng.random() < 0.5 else -hi
+        x = x.astype(F32)
+        if over:
+            x[0] = F32(2.0 ** -149)  # the smallest subnormal
+        out.append(x)
+        kind.append("over" if over else "finite")
+    return np.concatenate(out), kind
+
+
+def pin_tiny_scales(O):
+    """Blocks whose reciprocal 1/step overflows fp32 are sent as zero codes and, with
+    beta = 0 (Eqn. (4)), leave the new error equal to h exactly; blocks just above that
+    range (a subnormal step with a finite reciprocal) are still quantised within the
+    rounding bound, with the largest element at +-qmax; exact zeros code to 0; nothing is
+    NaN or infinite."""
+    rng = _rng(60)
+    for bits, block in ((4, 64), (8, 128), (2, 64)):
+        qmax = (1 << (bits - 1)) - 1
+        g, kind = _tiny_blocks(rng, block, qmax, 9)
+        out = O.compensate_quantize(g, np.zeros(g.size, F32), bits=bits, block=block, beta=0.0)
+        assert np.all(np.isfinite(out["e_new"])) and np.all(np.isfinite(out["d"]))
+        q = out["q"]
+        assert q.min() >= -qmax - 1 and q.max() <= qmax
+        for b, kd in enumerate(kind):
+            sl = slice(b * block, (b + 1) * block)
+            hb, qb = g[sl].astype(np.float64), q[sl]
+            am = float(out["absmax"][b])
+            assert am == np.abs(hb).max()
+            if kd in ("zero", "over"):
+                if kd == "over":
+                    assert 1.0 / (am / qmax) >= 4 * _F32_OVERFLOW  # far inside the overflow range
+                assert not np.any(qb), (bits, b, kd)
+                assert np.array_equal(out["e_new"][sl].view(np.uint32), g[sl].view(np.uint32)), (bits, b)
+            else:
+                assert 1.0 / (am / qmax) <= 2.0 ** 127  # comfortably finite
+                # step = fl(am / qmax) is subnormal (>= 2^-127): its relative rounding is
+                # at most 2^-23; with the roundings of 1/step, h * inv and q * step
+                # (half a subnormal ulp, 2^-150, or 2^-24 relative) the bound below holds
+                step = am / qmax
+                assert step < 2.0 ** -126
+                bound = step * (0.5 + qmax * 2.0 ** -20) + 2.0 ** -149
+                r = np.abs(hb - out["d"][sl].astype(np.float64))
+                assert np.all(r <= bound), (bits, b, r.max(), bound)
+                assert np.abs(qb).max() == qmax, (bits, b)
+            zeros = hb == 0
+            assert not np.any(qb[zeros]) and not np.any(out["e_new"][sl][zeros])
+
+
+def pin_topk_tiny_scales(O):
+    """Top-k on chunks of tiny values: a chunk whose kept absmax is too small for a finite
+    1/step keeps the right indices, sends zero codes and feeds every value back whole
+    (e' = h everywhere); a chunk with a subnormal but invertible step quantises its largest
+    kept value to +-qmax."""
+    rng = _rng(61)
+    for bits in (2, 4):
+        qmax = (1 << (bits - 1)) - 1
+        chunk, k = 64, 5
+        g, kind = _tiny_blocks(rng, chunk, qmax, 5)
+        r = O.topk_quantize(g, np.zeros(g.size, F32), chunk=chunk, k=k, bits=bits, decay=1.0)
+        assert np.all(np.isfinite(r["e_new"]))
+        q = O.unpack_codes(r["codes"], bits, r["codes"].size * 8 // bits).reshape(len(kind), -1)[:, :k]
+        for c, kd in enumerate(kind):
+            sl = slice(c * chunk, (c + 1) * chunk)
+            key = np.abs(g[sl]).view(np.uint32)
+            assert np.array_equal(r["idx"][c * k:(c + 1) * k], _brute_topk(key, k).astype(np.uint16))
+            if kd in ("zero", "over"):
+                assert not np.any(q[c]), (bits, c)
+                assert np.array_equal(r["e_new"][sl].view(np.uint32), g[sl].view(np.uint32))
+            else:
+                assert np.abs(q[c]).max() == qmax, (bits, c, q[c])
+
+
 ALL_PINS = [
     pin_identity_compressor, pin_beta_zero_is_efc, pin_quantisation_bound,
     pin_random_walk_bounded, pin_telescoping, pin_fixed_scale_golden, pin_torch_quantiser,
@@ -666,4 +780,5 @@ ALL_PINS = [
     pin_i8_error_accounting, pin_i8_equals_float_when_exact, pin_reset, pin_i8_compressor_vs_torch,
     pin_sa_worked, pin_sa_brute_force, pin_sa_dense_equivalent, pin_sa_transmits_topk,
     pin_adam_worked, pin_adam_closed_form, pin_adam_limits, pin_cq_scalar_twin, pin_dr_scalar_twin,
+    pin_dra_worked, pin_tiny_scales, pin_topk_tiny_scales,
 ]

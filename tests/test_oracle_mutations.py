@@ -165,6 +165,47 @@ def _adam_bias_corrected(theta, m, v, g, *, lr, beta1, beta2, delta, ftype=np.fl
     return theta - ft(lr) * (mh / np.sqrt(vh + ft(delta))), m_new, v_new
 
 
+def _dra_bf16_gradient(payloads, n, **kw):
+    # the averaged gradient rounded to bf16 before the step
+    g = _orig["dequant_reduce"](payloads, n, bits=kw["bits"], block=kw["block"], out_scale=kw["out_scale"],
+                                out_dtype="bf16", fixed_scale=kw.get("fixed_scale", 0.0))
+    g = _orig["bf16_to_f32"](g)
+    th, m, v = _orig["adam_step"](kw["theta"], kw["m"], kw["v"], g, lr=kw["lr"], beta1=kw["beta1"],
+                                  beta2=kw["beta2"], delta=kw["delta"])
+    return {"theta": th, "m": m, "v": v, "g": g, "theta_bf16": _orig["bf16_rne"](th)}
+
+
+def _dra_scale_after(payloads, n, **kw):
+    # the step taken on the peers' sum, out_scale applied to the update afterwards
+    g = _orig["dequant_reduce"](payloads, n, bits=kw["bits"], block=kw["block"], out_scale=1.0,
+                                fixed_scale=kw.get("fixed_scale", 0.0))
+    th, m, v = _orig["adam_step"](kw["theta"], kw["m"], kw["v"], g, lr=kw["lr"] * kw["out_scale"],
+                                  beta1=kw["beta1"], beta2=kw["beta2"], delta=kw["delta"])
+    return {"theta": th, "m": m, "v": v, "g": g * np.float32(kw["out_scale"]), "theta_bf16": _orig["bf16_rne"](th)}
+
+
+def _dra_copy_truncated(payloads, n, **kw):
+    r = _orig["dequant_reduce_adam"](payloads, n, **kw)
+    r["theta_bf16"] = _bf16_truncate(r["theta"])
+    return r
+
+
+def _recip_keeps_overflow(step):
+    # only an all-zero block gets inv = 0; a tiny one keeps 1/step = inf
+    step = np.asarray(step)
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = step.dtype.type(1) / step
+    return np.where(step != 0, inv, step.dtype.type(0)).astype(step.dtype)
+
+
+def _recip_zero_subnormal(step):
+    # inv = 0 for every subnormal step, even where 1/step is finite
+    step = np.asarray(step)
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = step.dtype.type(1) / step
+    return np.where(step >= np.finfo(step.dtype).tiny, inv, step.dtype.type(0)).astype(step.dtype)
+
+
 MUTATIONS = {
     "error_update drops beta*e": ("error_update", _drop_beta_term),
     "error_update swaps beta and 1-beta": ("error_update", _swap_weights),
@@ -190,6 +231,11 @@ MUTATIONS = {
     "Adam with beta1 weighting the old moment": ("adam_step", _adam_swapped),
     "Adam with delta outside the square root": ("adam_step", _adam_delta_outside),
     "Adam with bias correction": ("adam_step", _adam_bias_corrected),
+    "Adam on the bf16-rounded average": ("dequant_reduce_adam", _dra_bf16_gradient),
+    "out_scale applied after the Adam step": ("dequant_reduce_adam", _dra_scale_after),
+    "bf16 weight copy truncated": ("dequant_reduce_adam", _dra_copy_truncated),
+    "tiny block keeps an infinite reciprocal": ("finite_reciprocal", _recip_keeps_overflow),
+    "reciprocal zeroed for every subnormal step": ("finite_reciprocal", _recip_zero_subnormal),
 }
 
 
