@@ -2,7 +2,8 @@
 //
 // LoCo ("LoCo: Low-Bit Communication Adaptor for Large-scale Model Training"),
 // Sec. 3.1 Eqns. (1)-(3) and Sec. 3.2 Eqns. (4)-(5), with a per-block absmax scale:
-//   h = g + e;  absmax = max|h| per block;  step = absmax/qmax;  inv = 1/step
+//   h = g + e;  absmax = max|h| per block;  step = absmax/qmax;  inv = 1/step (0 where
+//   that is not finite: an all-zero block, or one too small for its reciprocal)
 //   q = clamp(rint(h*inv));  r = h - q*step;  e' = beta*e + (1-beta)*r
 // The error is stored as fp32, bf16, or the paper's 8-bit codes of a fixed scale s_e
 // (Sec. 3.2, Eqn. (7): e = e8 * fl(1/s_e) on load, e8' = clamp(rint(e' * s_e)) on store),
@@ -180,7 +181,7 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
                 mb = (lane / BPS == u) ? v : mb;
             }
             const float stepb = __uint_as_float(mb) / (float)QMAX;
-            const float invb = (mb != 0u) ? 1.0f / stepb : 0.0f;
+            const float invb = finite_recip(stepb);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int src = u * BPS + lane / LPB;
@@ -191,7 +192,7 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 step_u[u] = am_u[u] / (float)QMAX;
-                inv_u[u] = (mu[u] != 0u) ? 1.0f / step_u[u] : 0.0f;
+                inv_u[u] = finite_recip(step_u[u]);
             }
         }
     }

@@ -43,6 +43,17 @@ __device__ __forceinline__ float ubyte_to_f32(uint32_t x) {
     return r;
 }
 
+// ---- block scales ----------------------------------------------------------------
+
+// The quantiser's reciprocal inv = fl(1/step) (correctly rounded by build flag), or 0 where
+// it is not finite: step = 0 (an all-zero block) or step below ~2^-128, where 1/step
+// overflows fp32.  Such a block cannot be scaled into the code range; with inv = 0 every
+// code is 0 and error feedback keeps the block's values whole.
+__device__ __forceinline__ float finite_recip(float step) {
+    const float r = 1.0f / step;
+    return r < __builtin_huge_valf() ? r : 0.0f;
+}
+
 // ---- code packing -----------------------------------------------------------------
 
 // Eight BITS-bit two's-complement codes q[j] (integer-valued floats in [-2^(BITS-1),

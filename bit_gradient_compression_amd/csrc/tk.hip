@@ -215,7 +215,7 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
     const uint32_t M = max(max(sh.wmax[0], sh.wmax[1]), max(sh.wmax[2], sh.wmax[3]));
     const float absmax = __uint_as_float(M);
     const float step = absmax / (float)QMAX;
-    const float inv = (M != 0u) ? 1.0f / step : 0.0f;
+    const float inv = finite_recip(step);  // 0 for a zero chunk or one too small to scale
 
     bool fast = false;
     if (keff <= kTkThreads) {

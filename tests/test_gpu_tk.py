@@ -90,17 +90,80 @@ def test_tk_zero_chunks(gpu_lib):
     run_tk_chain(gpu_lib, 3 * 4096 + 500, 4096, 82, 2, 1.0, 3, gen, "zeros")
 
 
+# Host model of the kernel's routing at chunk 4096 (256 threads, thread t holding the 16
+# elements q*1024 + 4t + r): the lower bound L is the largest key with only bits 30..19 set
+# that at least k per-thread maxima reach; the keys >= L are the candidates, and the fast
+# path takes a chunk when they fit the 512-slot list.
+TK_CAP = 512
+
+
+def fast_path_candidates(h_chunk, k):
+    key = np.abs(np.asarray(h_chunk, np.float32)).view(np.uint32)
+    per_thread = key.reshape(4, 256, 4).transpose(1, 0, 2).reshape(256, 16).max(axis=1)
+    L = 0
+    for bit in range(30, 18, -1):
+        cand = L | (1 << bit)
+        if np.count_nonzero(per_thread >= cand) >= k:
+            L = cand
+    return int(np.count_nonzero(key >= L))
+
+
 def test_tk_fallback_layout(gpu_lib):
-    """Large values only in lanes 0..9 of every slot: the per-lane top-2 bound admits more
-    than the candidate capacity, so the kernel takes its exhaustive path."""
+    """Large values only in lanes 0..9 of every 64-element row: per-thread maxima give a
+    low bound, more keys than the 512-slot candidate list reach it, and the kernel takes
+    its exhaustive path (asserted on the host model of its routing)."""
     def gen(step, n):
         x = W.sparseloco_grad(step, n=n)
         i = torch.arange(n)
         big = (i % 64) < 10
         x[big] = x[big] * 50 + torch.sign(x[big]) * 0.05
         return x
+    x = gen(0, 6 * 4096).numpy()  # step 0: e = 0, so h = g
+    assert min(fast_path_candidates(x[c * 4096:(c + 1) * 4096], 82) for c in range(6)) > TK_CAP
     say("tk fallback layout")
     run_tk_chain(gpu_lib, 6 * 4096, 4096, 82, 2, 1.0, 3, gen, "fallback")
+
+
+def fast_ties_gen(step, n):
+    """Per 4096-element chunk: 40 elements at exactly +-0.1 and 200 at exactly +-0.05, each
+    in a different thread's 16 elements (240 random threads of 256), the rest N(0, 1e-3)."""
+    rng = np.random.default_rng([4242, step])
+    x = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    for c in range(n // 4096):
+        threads = rng.permutation(256)[:240]
+        q = rng.integers(0, 4, 240)
+        r = rng.integers(0, 4, 240)
+        pos = c * 4096 + q * 1024 + 4 * threads + r
+        sgn = np.where(rng.random(240) < 0.5, -1.0, 1.0).astype(np.float32)
+        x[pos[:40]] = np.float32(0.1) * sgn[:40]
+        x[pos[40:]] = np.float32(0.05) * sgn[40:]
+    return torch.from_numpy(x)
+
+
+@pytest.mark.parametrize("k", [41, 82, 150])
+def test_tk_fast_path_ties(gpu_lib, k):
+    """Many equal magnitudes at the threshold on the fast path: k - 40 of the 200 ties at
+    0.05 are kept, the lower indices first.  The host model of the kernel's routing shows
+    every chunk on the fast path (at most 512 candidates) with the kept ties ending past
+    the first 64-slot candidate group in some chunk.  Decay 0.5 keeps the leftover ties'
+    error (0.025) below the next step's bound."""
+    n, C = 8 * 4096, 4096
+    e = np.zeros(n, np.float32)
+    crossed = False
+    for step in range(2):
+        x = fast_ties_gen(step, n).numpy()
+        h = x + np.float32(0.5) * e
+        for c in range(n // C):
+            hc = h[c * C:(c + 1) * C]
+            assert fast_path_candidates(hc, k) <= TK_CAP, (step, c)
+            key = np.abs(hc).view(np.uint32)
+            cand = np.flatnonzero(key >= np.abs(np.float32(0.05)).view(np.uint32))
+            kept = oracle.topk_order_select(key, k)
+            crossed |= int(np.searchsorted(cand, kept.max())) >= 64
+        e = oracle.topk_quantize(x, e, chunk=C, k=k, bits=2, decay=0.5)["e_new"]
+    assert crossed
+    say(f"tk fast-path ties k={k}")
+    run_tk_chain(gpu_lib, n, C, k, 2, 0.5, 2, fast_ties_gen, f"fast ties k{k}")
 
 
 def test_tk_small_tail_only(gpu_lib):
