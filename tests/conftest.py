@@ -21,3 +21,15 @@ def gpu_lib():
     from bit_gradient_compression_amd import loco
     loco.load()
     return loco
+
+
+@pytest.fixture(scope="session")
+def oracle_pool():
+    """Spawned worker processes (one per core, at most 16) that run the unchanged oracle on
+    slabs of the full-size workloads (tests/fullsize_pool.py).  Spawned, not forked: no
+    worker inherits the GPU runtime, and none imports torch."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    with ProcessPoolExecutor(min(16, cores), mp_context=multiprocessing.get_context("spawn")) as pool:
+        yield pool
