@@ -214,6 +214,7 @@ int dr_setup(const loco_payload_t* peers, int npeers, int64_t n, int bits, int b
         p.peer[i].codes = peers[i].codes;
         p.peer[i].absmax = peers[i].absmax;
     }
+    for (int i = npeers; i < npeers + kDrPeerBatch; ++i) p.peer[i] = p.peer[npeers - 1];
     p.npeers = npeers;
     p.n = n;
     p.fixed_step = fixed ? 1.0f / fixed_scale : 0.0f;
@@ -357,6 +358,7 @@ LOCO_API int loco_sparse_aggregate(const loco_sparse_payload_t* peers, int npeer
         p.peer[i].codes = peers[i].codes;
         p.peer[i].absmax = peers[i].absmax;
     }
+    for (int i = npeers; i < npeers + kDrPeerBatch; ++i) p.peer[i] = p.peer[npeers - 1];
     p.npeers = npeers;
     p.k = k;
     p.cbytes = (int)code_bytes(k, bits);

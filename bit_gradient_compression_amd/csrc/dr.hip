@@ -25,13 +25,20 @@
 namespace loco {
 namespace {
 
-// Codes of 8 consecutive elements (element i0 is a multiple of 8): 2, 4 or 8 bytes.
+// A raw buffer resource over `bytes` bytes at p.  Loads through it take the base from
+// SGPRs and a 32-bit lane offset (no per-lane 64-bit address arithmetic), and an offset
+// past `bytes` reads 0 without touching memory.  Word 3 is gfx9's raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kLoadNt = 2;  // cache-policy bit of a non-temporal (streaming) load on gfx950
+
+// Codes of 8 consecutive elements (2, 4 or 8 bytes) at byte offset off of a peer's tile.
 template <int BITS>
-__device__ __forceinline__ u32x2 load_codes8(const uint8_t* c, int64_t i0) {
-    const uint8_t* p = c + (i0 * BITS) / 8;
-    if constexpr (BITS == 2) return u32x2{(uint32_t)__builtin_nontemporal_load((const uint16_t*)p), 0u};
-    else if constexpr (BITS == 4) return u32x2{__builtin_nontemporal_load((const uint32_t*)p), 0u};
-    else return __builtin_nontemporal_load((const u32x2*)p);
+__device__ __forceinline__ u32x2 load_codes_at(__amdgpu_buffer_rsrc_t tile, uint32_t off) {
+    if constexpr (BITS == 2) return u32x2{(uint32_t)__builtin_amdgcn_raw_buffer_load_b16(tile, off, 0, kLoadNt), 0u};
+    else if constexpr (BITS == 4) return u32x2{__builtin_amdgcn_raw_buffer_load_b32(tile, off, 0, kLoadNt), 0u};
+    else return __builtin_amdgcn_raw_buffer_load_b64(tile, off, 0, kLoadNt);
 }
 
 // Signed code j (0..7) of the 8 held in w.
@@ -163,40 +170,51 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                 }
             }
             // whole wave tile in range.  The tile spans BPT scale blocks; the steps of G
-            // peers x BPT blocks are computed one per lane (one division per lane per G
-            // peers) and each lane fetches its block's step with a lane shuffle.
+            // peers x BPT blocks are computed one per lane (lane l divides peer l / BPT's
+            // block l % BPT: one division per lane per G peers) and each lane fetches its
+            // block's step with ds_bpermute.  Every payload load goes through a buffer
+            // resource over the peer's part of the tile (its base in SGPRs, a 32-bit lane
+            // offset).
             constexpr int BPT = TILE / B;
             constexpr int G = 64 / BPT;
+            constexpr int CB = kDrVec * BITS / 8;  // code bytes per lane per sub-tile
             const int64_t blk0 = t * (TILE / B);
+            const int64_t cbase = t * (int64_t)(TILE * BITS / 8);
+            const uint32_t coff = (uint32_t)lane * CB;
+            const uint32_t aoff = (uint32_t)(lane % BPT) * 4u;
+            const int myq = lane / BPT;
             int myblk[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) myblk[u] = (int)((base + u * SUB) / B - blk0);
             for (int pg = 0; pg < p.npeers; pg += G) {
                 const int ng = p.npeers - pg < G ? p.npeers - pg : G;
                 // codes of a batch of peers, all loads in flight together (slots past the
-                // group re-read its last peer and are not accumulated)
+                // group read later peers or the table's copies of the last one, and are
+                // not accumulated)
                 u32x2 w[kDrPeerBatch][U];
                 auto load_batch = [&](int q0) {
 #pragma unroll
                     for (int b = 0; b < kDrPeerBatch; ++b) {
-                        const int q = q0 + b < ng ? q0 + b : ng - 1;
-                        const uint8_t* codes = p.peer[pg + q].codes;
+                        const auto ct = buffer_rsrc(p.peer[pg + q0 + b].codes + cbase, TILE * BITS / 8);
 #pragma unroll
-                        for (int u = 0; u < U; ++u) w[b][u] = load_codes8<BITS>(codes, base + u * SUB);
+                        for (int u = 0; u < U; ++u) w[b][u] = load_codes_at<BITS>(ct, coff + u * (SUB * BITS / 8));
                     }
                 };
                 load_batch(0);  // issued before the scales, so both latencies overlap
                 float stp = p.fixed_step;
                 if constexpr (!FIXED) {
                     constexpr int QMAX = (1 << (BITS - 1)) - 1;
-                    // every lane loads its block's absmax of each peer of the group and keeps
-                    // the one of its own peer: one division per lane per group
+                    // every lane loads its block's absmax of each peer of a batch and keeps
+                    // the one of its own peer
                     float am = 0.0f;
+                    for (int q0 = 0; q0 < ng; q0 += kDrPeerBatch) {
+                        float a[kDrPeerBatch];
 #pragma unroll
-                    for (int q = 0; q < G; ++q) {
-                        const int qq = q < ng ? q : ng - 1;
-                        const float v = p.peer[pg + qq].absmax[blk0 + lane % BPT];
-                        am = (lane / BPT == q) ? v : am;
+                        for (int b = 0; b < kDrPeerBatch; ++b)
+                            a[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                buffer_rsrc(p.peer[pg + q0 + b].absmax + blk0, BPT * 4), aoff, 0, 0));
+#pragma unroll
+                        for (int b = 0; b < kDrPeerBatch; ++b) am = (myq == q0 + b) ? a[b] : am;
                     }
                     stp = am / (float)QMAX;  // 0 for an all-zero block
                 }

@@ -118,7 +118,9 @@ struct DrPeerDev {
 };
 
 struct DrParams {
-    DrPeerDev peer[kDrMaxPeers];
+    // Entries npeers .. npeers + kDrPeerBatch - 1 repeat the last peer, so a batch of
+    // loads past the last peer reads valid memory and needs no bounds branch.
+    DrPeerDev peer[kDrMaxPeers + kDrPeerBatch];
     int npeers;
     int64_t n;
     int64_t ntiles;
