@@ -21,6 +21,10 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libloco.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["abi.hip", "cq.hip", "dr.hip", "tk.hip", "sa.hip"]
+# Traffic twins of the kernels, for the benchmark only: a library of their own, outside
+# the API that include/loco.h declares.
+TWINS_SOURCES = ["twins.hip"]
+TWINS_PATH = os.path.join(PKG, "libloco_twins.so")
 ARCH = "gfx950"
 
 
@@ -47,14 +51,15 @@ def _run(cmd):
 
 
 def build(out_path: str = LIB_PATH, extra_flags=(), jobs: int | None = None, verbose=False,
-          build_dir: str = BUILD_DIR) -> str:
-    """Compile and link the library; returns the path of the .so."""
+          build_dir: str = BUILD_DIR, twins_path: str | None = TWINS_PATH) -> str:
+    """Compile and link the library (and, unless twins_path is None, the benchmark's
+    traffic twins); returns the path of the library's .so."""
     os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
     flags = compile_flags(extra_flags)
     objs = []
     cmds = []
-    for src in SOURCES:
+    for src in SOURCES + (TWINS_SOURCES if twins_path else []):
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
@@ -63,9 +68,13 @@ def build(out_path: str = LIB_PATH, extra_flags=(), jobs: int | None = None, ver
         for r in ex.map(_run, cmds):
             if verbose and r.stderr:
                 print(r.stderr, file=sys.stderr)
-    tmp = out_path + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, out_path)
+    links = [(out_path, objs[:len(SOURCES)])]
+    if twins_path:
+        links.append((twins_path, objs[len(SOURCES):]))
+    for path, os_ in links:
+        tmp = path + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *os_, "-o", tmp])
+        os.replace(tmp, path)
     return out_path
 
 

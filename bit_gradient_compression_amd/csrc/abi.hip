@@ -358,7 +358,6 @@ LOCO_API int loco_sparse_aggregate(const loco_sparse_payload_t* peers, int npeer
         p.peer[i].codes = peers[i].codes;
         p.peer[i].absmax = peers[i].absmax;
     }
-    for (int i = npeers; i < npeers + kDrPeerBatch; ++i) p.peer[i] = p.peer[npeers - 1];
     p.npeers = npeers;
     p.k = k;
     p.cbytes = (int)code_bytes(k, bits);

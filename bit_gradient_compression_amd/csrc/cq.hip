@@ -10,16 +10,19 @@
 // and a step may store e' = 0 instead (the periodic reset of Eqn. (7)).
 //
 // Mapping: a wavefront owns a tile of sub-tiles of 512 elements (one sub-tile with a
-// float error, two with an 8-bit error, whose waves move fewer bytes); lane l owns 8
-// consecutive elements of each sub-tile, so one bf16 gradient load, two fp32 error loads
-// (one 8-byte load of an 8-bit error) and one 32-bit code store per lane are coalesced.
-// A scale block of B elements is B/8 consecutive lanes; its absmax is reduced with DPP
-// row operations (and a permlane swap past 16 lanes).  Every load of a tile is issued
-// before any arithmetic.  The 8-bit-error kernel is bound by VALU issue as much as by
+// float error, two with an 8-bit error, whose waves move fewer bytes); lane l owns two
+// pieces of 4 consecutive elements of each sub-tile, at 4l and 256 + 4l, so that every
+// load and store instruction of the wave covers one contiguous run of memory (1 KB of an
+// fp32 error, 512 B of a bf16 gradient, 128 B of 4-bit codes).  The error is loaded and
+// stored non-temporally.  A scale block of B <= 256 elements is B/4 consecutive lanes of
+// one piece (a block of 512, both pieces of the wave); its absmax is reduced with DPP row
+// operations (and permlane swaps past 16 lanes).  Every load of a tile is issued before
+// any arithmetic.  The 8-bit-error kernel is bound by VALU issue as much as by
 // HBM, so its per-element work is kept to a minimum: codes are packed from the float q
 // with v_cvt_pk_u8_f32, the int8 error is encoded by a magic-number add and v_perm, and
-// a wave issues the two divisions of its blocks once for both sub-tiles (each lane
-// divides for one block; the results are shuffled to the block's lanes).
+// a wave issues the two divisions of its blocks once for all of its blocks (lane b
+// divides for block b and stores its absmax; the results are shuffled to the blocks'
+// lanes).
 // The grid covers all wave tiles of all segments of the call: each wave takes one tile
 // and exits, so the waves in flight sweep the buffers in address order (measured on
 // MI355X, a persistent grid-stride loop over the same traffic mix runs ~15% slower).
@@ -65,187 +68,286 @@ __device__ __forceinline__ void i8x4_to_f32(uint32_t w, float estep, float off, 
     x[3] = __builtin_fmaf(ubyte_to_f32<3>(u), estep, off);
 }
 
-// 8 consecutive elements starting at i0 (16-byte aligned for 2- and 4-byte kinds, 8-byte
-// for int8).  NT: non-temporal (the gradient is read once).
-template <int K, bool NT>
-__device__ __forceinline__ void load8(const void* p, int64_t i0, float (&x)[8], float estep) {
-    if constexpr (K == kBF16) {
-        const u32x4* q = (const u32x4*)((const uint16_t*)p + i0);
-        const u32x4 w = NT ? __builtin_nontemporal_load(q) : *q;
-        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-    } else if constexpr (K == kI8) {
-        const u32x2* q = (const u32x2*)((const int8_t*)p + i0);
-        const u32x2 w = NT ? __builtin_nontemporal_load(q) : *q;
-        const float off = -128.0f * estep;
-        i8x4_to_f32(w.x, estep, off, x);
-        i8x4_to_f32(w.y, estep, off, x + 4);
-    } else {
-        const f32x4* q = (const f32x4*)((const float*)p + i0);
-        const f32x4 a = NT ? __builtin_nontemporal_load(q) : q[0];
-        const f32x4 b = NT ? __builtin_nontemporal_load(q + 1) : q[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
+// Lane layout of a 512-element sub-tile.  Each lane owns 8 elements as two pieces of 4
+// consecutive elements.  Split: the pieces sit at 4l and 256 + 4l, so every load and
+// store instruction of the wave covers one contiguous run (1 KB of an fp32 stream).
+// Contiguous: the lane's 8 elements are consecutive (8l), which already makes each
+// instruction contiguous when every stream has at most 2 bytes per element (bf16
+// gradient with a bf16 or 8-bit error).  The split layout is taken when the gradient or
+// the error is fp32: there, the contiguous layout makes each 16-byte instruction touch
+// half of every 32 bytes, and on MI355X the 7B shard's mix (bf16 gradient, fp32 error)
+// then streams at 5.67 TB/s in its traffic twin against 6.0 TB/s split.  The 8-bit-error
+// kernel is bound by instruction issue, and the split layout's extra reductions and
+// narrower accesses cost it 7% (0.663 against 0.622 ms).
+template <int GK, int EK>
+struct CqLayout {
+    static constexpr bool kSplit = GK == kF32 || EK == kF32;
+    // element offset, within the sub-tile, of piece pc of lane l
+    static __device__ __forceinline__ int piece(int l, int pc) { return kSplit ? pc * 256 + l * 4 : l * 8 + pc * 4; }
+};
+
+// Cache policy of the error stream: loaded and stored non-temporally (read once, written
+// once per step).  Split layout: 6.0 TB/s in the 7B shard's twin against 5.6 with plain
+// loads.  Contiguous layout: the MoE experts (bf16 error) 1.466 against 1.49 ms back to
+// back; the 8-bit error unchanged.
+#ifndef LOCO_CQ_E_LOAD_NT_SPLIT
+#define LOCO_CQ_E_LOAD_NT_SPLIT 1
+#endif
+#ifndef LOCO_CQ_E_LOAD_NT_CONTIG
+#define LOCO_CQ_E_LOAD_NT_CONTIG 1
+#endif
+
+template <class T, bool NT>
+__device__ __forceinline__ T ld(const void* p) {
+    if constexpr (NT) return __builtin_nontemporal_load((const T*)p);
+    else return *(const T*)p;
 }
 
-// 8 consecutive elements of the new error; zero: store 0 instead (the error reset).
-template <int K>
-__device__ __forceinline__ void store8(void* p, int64_t i0, const float (&x)[8], float escale, bool zero) {
+// N = 4 or 8 consecutive elements starting at i0 (i0 a multiple of N).  NT: non-temporal.
+template <int K, int N, bool NT>
+__device__ __forceinline__ void loadn(const void* p, int64_t i0, float* x, float estep, float eoff) {
     if constexpr (K == kBF16) {
-        u32x4 w;
-        w.x = bf16x2_rne(x[0], x[1]); w.y = bf16x2_rne(x[2], x[3]);
-        w.z = bf16x2_rne(x[4], x[5]); w.w = bf16x2_rne(x[6], x[7]);
-        if (zero) w = u32x4{0u, 0u, 0u, 0u};
-        __builtin_nontemporal_store(w, (u32x4*)((uint16_t*)p + i0));
-    } else if constexpr (K == kI8) {
-        u32x2 w = {low_bytes4(i8_code_bits(x[0], escale), i8_code_bits(x[1], escale), i8_code_bits(x[2], escale),
-                              i8_code_bits(x[3], escale)),
-                   low_bytes4(i8_code_bits(x[4], escale), i8_code_bits(x[5], escale), i8_code_bits(x[6], escale),
-                              i8_code_bits(x[7], escale))};
-        if (zero) w = u32x2{0u, 0u};
-        __builtin_nontemporal_store(w, (u32x2*)((int8_t*)p + i0));
-    } else {
-        f32x4* q = (f32x4*)((float*)p + i0);
-        f32x4 a = {x[0], x[1], x[2], x[3]};
-        f32x4 b = {x[4], x[5], x[6], x[7]};
-        if (zero) {
-            a = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            b = a;
+        if constexpr (N == 8) {
+            const u32x4 w = ld<u32x4, NT>((const uint16_t*)p + i0);
+            x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+            x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+        } else {
+            const u32x2 w = ld<u32x2, NT>((const uint16_t*)p + i0);
+            x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
         }
-        __builtin_nontemporal_store(a, q);
-        __builtin_nontemporal_store(b, q + 1);
+    } else if constexpr (K == kI8) {
+        if constexpr (N == 8) {
+            const u32x2 w = ld<u32x2, NT>((const int8_t*)p + i0);
+            i8x4_to_f32(w.x, estep, eoff, x);
+            i8x4_to_f32(w.y, estep, eoff, x + 4);
+        } else {
+            i8x4_to_f32(ld<uint32_t, NT>((const int8_t*)p + i0), estep, eoff, x);
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < N / 4; ++v) {
+            const f32x4 a = ld<f32x4, NT>((const float*)p + i0 + 4 * v);
+            x[4 * v] = a.x; x[4 * v + 1] = a.y; x[4 * v + 2] = a.z; x[4 * v + 3] = a.w;
+        }
     }
 }
 
-template <int GK, int EK, int BITS, int B, bool FIXED, bool FULL>
+// N = 4 or 8 consecutive elements of the new error (non-temporal).  keep is all ones, or
+// 0 on a reset step (store 0 instead): a mask on the stored words, so that the step's
+// arithmetic stays branch-free.
+template <int K, int N>
+__device__ __forceinline__ void storen(void* p, int64_t i0, const float* x, float escale, uint32_t keep) {
+    if constexpr (K == kBF16) {
+        if constexpr (N == 8) {
+            const u32x4 w = {bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3]), bf16x2_rne(x[4], x[5]),
+                             bf16x2_rne(x[6], x[7])};
+            __builtin_nontemporal_store(w & keep, (u32x4*)((uint16_t*)p + i0));
+        } else {
+            const u32x2 w = {bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3])};
+            __builtin_nontemporal_store(w & keep, (u32x2*)((uint16_t*)p + i0));
+        }
+    } else if constexpr (K == kI8) {
+        uint32_t w[N / 4];
+#pragma unroll
+        for (int v = 0; v < N / 4; ++v)
+            w[v] = keep & low_bytes4(i8_code_bits(x[4 * v], escale), i8_code_bits(x[4 * v + 1], escale),
+                                     i8_code_bits(x[4 * v + 2], escale), i8_code_bits(x[4 * v + 3], escale));
+        if constexpr (N == 8) __builtin_nontemporal_store(u32x2{w[0], w[1]}, (u32x2*)((int8_t*)p + i0));
+        else __builtin_nontemporal_store(w[0], (uint32_t*)((int8_t*)p + i0));
+    } else {
+#pragma unroll
+        for (int v = 0; v < N / 4; ++v) {
+            const u32x4 a = {__float_as_uint(x[4 * v]), __float_as_uint(x[4 * v + 1]), __float_as_uint(x[4 * v + 2]),
+                             __float_as_uint(x[4 * v + 3])};
+            __builtin_nontemporal_store(a & keep, (u32x4*)((float*)p + i0) + v);
+        }
+    }
+}
+
+// The codes of N = 4 or 8 consecutive elements (N*BITS/8 bytes, low bits of lo:hi first)
+// at element i0 (a multiple of N).
+template <int BITS, int N>
+__device__ __forceinline__ void store_codes(uint8_t* codes, int64_t i0, uint32_t lo, uint32_t hi) {
+    uint8_t* c = codes + (i0 * BITS) / 8;
+    constexpr int NB = N * BITS / 8;
+    if constexpr (NB == 8) __builtin_nontemporal_store(u32x2{lo, hi}, (u32x2*)c);
+    else if constexpr (NB == 4) __builtin_nontemporal_store(lo, (uint32_t*)c);
+    else if constexpr (NB == 2) __builtin_nontemporal_store((uint16_t)lo, (uint16_t*)c);
+    else __builtin_nontemporal_store((uint8_t)lo, c);
+}
+
+// U sub-tiles of 512 elements from element `base` of the segment, in the lane layout of
+// CqLayout.  Element j < 4 of the lane is piece 0's j, element j >= 4 piece 1's j - 4.
+// FULL: all U sub-tiles are inside the segment; otherwise elements past its end are
+// neither read nor written.
+template <int GK, int EK, int BITS, int B, bool FIXED, bool FULL, int U>
 __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int lane,
                                         const CqParams& p) {
+    using LY = CqLayout<GK, EK>;
+    constexpr bool SPLIT = LY::kSplit;
     constexpr int QMAX = (1 << (BITS - 1)) - 1;
-    constexpr int LPB = B / kCqVec;  // lanes per scale block
     constexpr int SUB = 64 * kCqVec;
-    constexpr int U = cq_unroll(EK);
+    constexpr bool ENT = SPLIT ? LOCO_CQ_E_LOAD_NT_SPLIT != 0 : LOCO_CQ_E_LOAD_NT_CONTIG != 0;
     float h[U][kCqVec];
     float e[U][kCqVec];
+    const float eoff = -128.0f * p.err_step;  // the 8-bit error's decoder offset
 
     // Issue every load of the tile first.
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t i0 = base + u * SUB + lane * kCqVec;
         float g[kCqVec];
-        if constexpr (FULL) {
-            load8<GK, true>(sg.g, i0, g, 0.0f);
-            load8<EK, false>(sg.e, i0, e[u], p.err_step);
+        if constexpr (FULL && !SPLIT) {
+            const int64_t i0 = base + u * SUB + LY::piece(lane, 0);
+            loadn<GK, 8, true>(sg.g, i0, g, 0.0f, 0.0f);
+            loadn<EK, 8, ENT>(sg.e, i0, e[u], p.err_step, eoff);
         } else {
 #pragma unroll
-            for (int j = 0; j < kCqVec; ++j) {
-                const bool ok = i0 + j < sg.n;
-                g[j] = ok ? load1<GK>(sg.g, i0 + j, 0.0f) : 0.0f;
-                e[u][j] = ok ? load1<EK>(sg.e, i0 + j, p.err_step) : 0.0f;
+            for (int pc = 0; pc < 2; ++pc) {
+                const int64_t i0 = base + u * SUB + LY::piece(lane, pc);
+                if constexpr (FULL) {
+                    loadn<GK, 4, true>(sg.g, i0, g + 4 * pc, 0.0f, 0.0f);
+                    loadn<EK, 4, ENT>(sg.e, i0, e[u] + 4 * pc, p.err_step, eoff);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool ok = i0 + j < sg.n;
+                        g[4 * pc + j] = ok ? load1<GK>(sg.g, i0 + j, 0.0f) : 0.0f;
+                        e[u][4 * pc + j] = ok ? load1<EK>(sg.e, i0 + j, p.err_step) : 0.0f;
+                    }
+                }
             }
         }
 #pragma unroll
         for (int j = 0; j < kCqVec; ++j) h[u][j] = g[j] + e[u][j];  // Eqn. (2)
     }
 
-    // Block scales.  With several sub-tiles per wave, lane b takes the maximum of the
-    // tile's b-th block and divides once (step = absmax / qmax, inv = 1 / step); each lane
-    // then fetches its own block's pair: the same quotients, one division per block
-    // instead of one per lane.
-    constexpr int BPS = 64 / LPB;  // blocks per sub-tile
-    float step_u[U], inv_u[U], am_u[U];
+    // Block scales.  In the split layout a block of B <= 256 elements is B/4 consecutive
+    // lanes of one piece (a block of 512 is both pieces of all lanes); in the contiguous
+    // layout it is B/8 consecutive lanes.  The maxima of |h| are reduced over each block's
+    // lanes (DPP, permlane swaps); then lane b takes the tile's b-th block maximum,
+    // divides once (step = absmax / qmax, inv = 1 / step, 0 where not finite) and stores
+    // that block's absmax, and every lane fetches the step and inverse of its blocks:
+    // two divisions per lane per tile, whatever the number of blocks.
+    constexpr int BPS = SUB / B;  // blocks per sub-tile
+    constexpr int NB = U * BPS;   // blocks per tile (<= 16)
+    constexpr int LPB = SPLIT ? (B <= SUB / 2 ? B / 4 : 64) : B / 8;  // a block's lanes in a piece
+    float stepA[U], invA[U], stepB[U], invB[U];
     if constexpr (FIXED) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            step_u[u] = p.fixed_step;
-            inv_u[u] = p.fixed_inv;
-            am_u[u] = 0.0f;
+            stepA[u] = stepB[u] = p.fixed_step;
+            invA[u] = invB[u] = p.fixed_inv;
         }
     } else {
-        uint32_t mu[U];
+        uint32_t mA[U], mB[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // max |h| as a float (|x| is a free source modifier): for finite values the
             // same element, and the same bits, as the largest |h| bit pattern
-            float mf = 0.0f;
+            float fa = 0.0f, fb = 0.0f;
 #pragma unroll
-            for (int j = 0; j < kCqVec; ++j) mf = fmaxf(mf, fabsf(h[u][j]));
-            mu[u] = group_max_u32<LPB>(__float_as_uint(mf));
-            am_u[u] = __uint_as_float(mu[u]);
+            for (int j = 0; j < 4; ++j) {
+                fa = fmaxf(fa, fabsf(h[u][j]));
+                fb = fmaxf(fb, fabsf(h[u][4 + j]));
+            }
+            if constexpr (SPLIT && B <= SUB / 2) {
+                mA[u] = group_max_u32<LPB>(__float_as_uint(fa));
+                mB[u] = group_max_u32<LPB>(__float_as_uint(fb));
+            } else {
+                mA[u] = mB[u] = group_max_u32<LPB>(__float_as_uint(fmaxf(fa, fb)));
+            }
         }
-        if constexpr (U > 1) {
-            uint32_t mb = 0;
+        // lane b < NB: block b of the tile, block k = b % BPS of sub-tile b / BPS.  Split:
+        // piece 0's block k (k < BPS/2) or piece 1's block k - BPS/2, at lane
+        // (k % (BPS/2)) * LPB (a block of 512: lane 0).  Contiguous: lane k * LPB.
+        constexpr bool TWO = SPLIT && BPS >= 2;
+        const int k = lane % BPS;
+        const int src = TWO ? (k % (BPS / 2)) * LPB : k * LPB;
+        uint32_t mb = 0u;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t v = (uint32_t)__shfl((int)mu[u], (lane % BPS) * LPB, 64);
-                mb = (lane / BPS == u) ? v : mb;
+        for (int u = 0; u < U; ++u) {
+            const uint32_t va = (uint32_t)__shfl((int)mA[u], src, 64);
+            uint32_t v = va;
+            if constexpr (TWO) {
+                const uint32_t vb = (uint32_t)__shfl((int)mB[u], src, 64);
+                v = k >= BPS / 2 ? vb : va;
             }
-            const float stepb = __uint_as_float(mb) / (float)QMAX;
-            const float invb = finite_recip(stepb);
+            mb = (lane / BPS == u) ? v : mb;
+        }
+        const float amb = __uint_as_float(mb);
+        const float stepb = amb / (float)QMAX;
+        const float invb = finite_recip(stepb);
+        // the block's absmax, stored by its lane (blocks past a ragged end are skipped)
+        if (lane < NB) {
+            if (FULL || base + (int64_t)lane * B < sg.n) sg.absmax[base / B + lane] = amb;
+        }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int src = u * BPS + lane / LPB;
-                step_u[u] = __shfl(stepb, src, 64);
-                inv_u[u] = __shfl(invb, src, 64);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                step_u[u] = am_u[u] / (float)QMAX;
-                inv_u[u] = finite_recip(step_u[u]);
+        for (int u = 0; u < U; ++u) {
+            const int ba = u * BPS + LY::piece(lane, 0) / B;  // piece 0's block in the tile
+            stepA[u] = __shfl(stepb, ba, 64);
+            invA[u] = __shfl(invb, ba, 64);
+            if constexpr (SPLIT && B <= SUB / 2) {
+                const int bb = u * BPS + LY::piece(lane, 1) / B;  // piece 1's block
+                stepB[u] = __shfl(stepb, bb, 64);
+                invB[u] = __shfl(invb, bb, 64);
+            } else {
+                stepB[u] = stepA[u];
+                invB[u] = invA[u];
             }
         }
     }
 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t i0 = base + u * SUB + lane * kCqVec;
-        const float step = step_u[u], inv = inv_u[u], am = am_u[u];
-
         float en[kCqVec], rq[kCqVec];
 #pragma unroll
         for (int j = 0; j < kCqVec; ++j) {
+            const float step = j < 4 ? stepA[u] : stepB[u];
+            const float inv = j < 4 ? invA[u] : invB[u];
             const float x = h[u][j] * inv;
             rq[j] = __builtin_amdgcn_fmed3f(__builtin_rintf(x), (float)(-QMAX - 1), (float)QMAX);
             const float d = rq[j] * step;                        // decompressor (rq is the integer q)
             const float r = h[u][j] - d;                         // Eqn. (4)
             en[j] = p.beta * e[u][j] + p.omega * r;              // Eqn. (5)
         }
+        // packed codes: element j of the lane at bits [BITS*j, BITS*j + BITS) of lo:hi, so
+        // piece 0's 4 codes are the low 4*BITS bits and piece 1's the next 4*BITS
         uint32_t packed_lo, packed_hi;
         pack_codes8<BITS>(rq, packed_lo, packed_hi);
-        const bool zero = p.reset;  // Eqn. (7): this step stores a zero error
-
-        if constexpr (FULL) {
-            store8<EK>(sg.e, i0, en, p.err_scale, zero);
-            uint8_t* c = sg.codes + (i0 * BITS) / 8;
-            if constexpr (BITS == 8) {
-                u32x2 w = {packed_lo, packed_hi};
-                __builtin_nontemporal_store(w, (u32x2*)c);
-            } else if constexpr (BITS == 4) {
-                __builtin_nontemporal_store(packed_lo, (uint32_t*)c);
-            } else {
-                __builtin_nontemporal_store((uint16_t)packed_lo, (uint16_t*)c);
-            }
-            if constexpr (!FIXED) {
-                if (lane % LPB == 0) sg.absmax[i0 / B] = am;
-            }
+        uint32_t cw[2];
+        if constexpr (BITS == 8) {
+            cw[0] = packed_lo;
+            cw[1] = packed_hi;
         } else {
-            const int64_t left = sg.n - i0;
-            const int nvalid = left <= 0 ? 0 : (left >= kCqVec ? kCqVec : (int)left);
+            cw[0] = packed_lo & ((1u << (4 * BITS)) - 1u);
+            cw[1] = packed_lo >> (4 * BITS);
+        }
+        const bool zero = p.reset;  // Eqn. (7): this step stores a zero error
+        const uint32_t keep = zero ? 0u : ~0u;
+
+        if constexpr (FULL && !SPLIT) {
+            const int64_t i0 = base + u * SUB + LY::piece(lane, 0);
+            storen<EK, 8>(sg.e, i0, en, p.err_scale, keep);
+            store_codes<BITS, 8>(sg.codes, i0, packed_lo, packed_hi);
+        } else {
 #pragma unroll
-            for (int j = 0; j < kCqVec; ++j)
-                if (j < nvalid) store1<EK>(sg.e, i0 + j, zero ? 0.0f : en[j], p.err_scale);
-            const int nbytes = (nvalid * BITS + 7) / 8;
-            uint8_t* c = sg.codes + (i0 * BITS) / 8;
+            for (int pc = 0; pc < 2; ++pc) {
+                const int64_t i0 = base + u * SUB + LY::piece(lane, pc);
+                if constexpr (FULL) {
+                    storen<EK, 4>(sg.e, i0, en + 4 * pc, p.err_scale, keep);
+                    store_codes<BITS, 4>(sg.codes, i0, cw[pc], 0u);
+                } else {
+                    const int64_t left = sg.n - i0;
+                    const int nvalid = left <= 0 ? 0 : (left >= 4 ? 4 : (int)left);
 #pragma unroll
-            for (int b = 0; b < kCqVec * BITS / 8; ++b) {
-                if (b < nbytes) {
-                    const uint32_t w = (b < 4) ? packed_lo : packed_hi;
-                    c[b] = (uint8_t)(w >> (8 * (b & 3)));
+                    for (int j = 0; j < 4; ++j)
+                        if (j < nvalid) store1<EK>(sg.e, i0 + j, zero ? 0.0f : en[4 * pc + j], p.err_scale);
+                    const int nbytes = (nvalid * BITS + 7) / 8;
+                    uint8_t* c = sg.codes + (i0 * BITS) / 8;
+#pragma unroll
+                    for (int b = 0; b < BITS / 2; ++b)
+                        if (b < nbytes) c[b] = (uint8_t)(cw[pc] >> (8 * b));
                 }
-            }
-            if constexpr (!FIXED) {
-                if (lane % LPB == 0 && nvalid > 0) sg.absmax[i0 / B] = am;
             }
         }
     }
@@ -273,10 +375,15 @@ __global__ __launch_bounds__(kCqThreads) void cq_kernel(CqParams p) {
          t += nwaves) {
         const CqSegDev sg = p.seg[find_segment(p, t)];
         const int64_t base = (t - sg.tile0) * TILE;
-        if (base + TILE <= sg.n)
-            cq_tile<GK, EK, BITS, B, FIXED, true>(sg, base, lane, p);
-        else
-            cq_tile<GK, EK, BITS, B, FIXED, false>(sg, base, lane, p);
+        if (base + TILE <= sg.n) {
+            cq_tile<GK, EK, BITS, B, FIXED, true, cq_unroll(EK)>(sg, base, lane, p);
+        } else {
+            // the segment's ragged last tile, one sub-tile at a time (a sub-tile holds whole
+            // blocks), so that its bounds checks do not raise the kernel's register count
+#pragma unroll 1
+            for (int u = 0; u < cq_unroll(EK) && base + u * 64 * kCqVec < sg.n; ++u)
+                cq_tile<GK, EK, BITS, B, FIXED, false, 1>(sg, base + u * 64 * kCqVec, lane, p);
+        }
     }
 }
 

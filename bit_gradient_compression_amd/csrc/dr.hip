@@ -122,9 +122,13 @@ __device__ __forceinline__ void adam1(const DrParams& p, float g, float& th, flo
     th = th - p.lr * (m * u);
 }
 
+#ifndef LOCO_DRA_NT_LOADS
+#define LOCO_DRA_NT_LOADS 0
+#endif
 __device__ __forceinline__ void load8f(const float* src, int64_t i0, float (&x)[kDrVec]) {
     const f32x4* q = (const f32x4*)(src + i0);
-    const f32x4 a = q[0], b = q[1];
+    const f32x4 a = LOCO_DRA_NT_LOADS ? __builtin_nontemporal_load(q) : q[0];
+    const f32x4 b = LOCO_DRA_NT_LOADS ? __builtin_nontemporal_load(q + 1) : q[1];
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }

@@ -32,6 +32,11 @@
 namespace loco {
 namespace {
 
+// The chunk's new error is stored non-temporally (written once, read again only by the
+// next step): 0.584 against 0.60 ms back to back on 2^28 with plain stores.
+#ifndef LOCO_TK_NT_ERR
+#define LOCO_TK_NT_ERR 1
+#endif
 constexpr int kTkThreads = 256;
 constexpr int kTkWaves = kTkThreads / kWave;
 // The lower bound L keeps key bits 30..kTkBoundLowBit (exponent + 4 mantissa bits).
@@ -448,7 +453,10 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
             const int i0 = q * ROW + tid * R;
             const uint32_t* hs = &sh.h[i0];
             if (FULL) {
-                if constexpr (R == 4) *(u32x4*)(eb + i0) = *(const u32x4*)hs;
+                if constexpr (R == 4) {
+                    if constexpr (LOCO_TK_NT_ERR) __builtin_nontemporal_store(*(const u32x4*)hs, (u32x4*)(eb + i0));
+                    else *(u32x4*)(eb + i0) = *(const u32x4*)hs;
+                }
                 else if constexpr (R == 2) *(u32x2*)(eb + i0) = *(const u32x2*)hs;
                 else *(uint32_t*)(eb + i0) = hs[0];
             } else {

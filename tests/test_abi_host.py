@@ -2,7 +2,10 @@
 declares, and refuses bad arguments on the host before any HIP call.
 
 Every call here either fails validation or has nothing to do (n == 0), so nothing is
-launched; the fake pointers are never dereferenced.
+launched; the fake pointers are never dereferenced.  The exception: calls with the most
+peers a call accepts pass validation and build their kernel arguments on the host, then
+fail to launch (no GPU here, LOCO_ERR_HIP); they check that building the peer tables
+stays inside them.
 """
 import ctypes
 import glob
@@ -265,6 +268,20 @@ def test_sa_peer_checks(lib):
     assert sa(lib, [spl()], n=0) == OK
     # a peer's scales inside the last 16 bytes of the output
     assert sa(lib, [spl(a=A + 10000 * 4 - 16)]) == INV
+
+
+HIP = loco.LOCO_ERR_HIP
+
+
+def test_max_peers_build_their_arguments(lib):
+    """128 peers (the maximum) pass validation and fill the kernel arguments' peer tables
+    on the host; with no GPU the launch then fails.  (A table written past its end on the
+    host stack crashed the process here.)"""
+    pls = [pl(Cp + i * 0x100000, Dp + i * 0x100000) for i in range(128)]
+    assert dr(lib, pls, n=1000) == HIP
+    assert dra(lib, pls, n=1000) == HIP
+    spls = [spl(Cp + i * 0x100000, Dp + i * 0x100000, 0x70000000 + i * 0x100000) for i in range(128)]
+    assert sa(lib, spls, n=10000) == HIP
 
 
 def dra(lib, peers, n=1000, bits=4, block=128, fixed=0.0, scale=0.25, hp=(1e-4, 0.1, 0.01, 1e-8), param=A,
