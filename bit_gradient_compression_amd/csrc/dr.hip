@@ -5,12 +5,13 @@
 // averages their decompressed values in high precision:
 //   acc = sum over p = 0..N-1 (in that order) of q_p * step_p;  out = acc * out_scale
 //
-// Mapping: a wave tile is kDrUnroll sub-tiles of 512 outputs; lane l owns 8 consecutive
-// outputs of each sub-tile, so every load of a peer's codes (4 bytes at 4 bits) and every
-// store of outputs (16 bytes of bf16, 32 of fp32) is contiguous across the wave and the
-// written lines are whole.  The 8 outputs of a lane sit in one scale block (blocks are
-// >= 64 elements).  The fp32 accumulator never leaves registers; only the reduced shard
-// is written.  One wave tile per wave, the grid covering all tiles.
+// Mapping: a wave tile is one or two sub-tiles of 512 outputs; lane l owns 8 outputs of
+// each sub-tile as two pieces of 4 consecutive elements (DrLayout): consecutive (8l) for
+// a bf16 shard, at 4l and 256 + 4l for an fp32 shard and the fused Adam step, so that
+// every load and store instruction of the wave covers one contiguous run.  A piece sits
+// in one scale block (blocks are >= 64 elements).  The fp32 accumulator never leaves
+// registers; only the reduced shard is written.  One wave tile per wave, the grid
+// covering all tiles.
 //
 // Fused consumer (LoCo, Sec. 4, Eqn. (9)): instead of writing the reduced gradient g,
 // the kernel takes one Adam-family step with it on the partition's fp32 weights and
@@ -33,11 +34,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
 }
 constexpr int kLoadNt = 2;  // cache-policy bit of a non-temporal (streaming) load on gfx950
 
-// Codes of 8 consecutive elements (2, 4 or 8 bytes) at byte offset off of a peer's tile.
-template <int BITS>
+// Codes of N = 4 or 8 consecutive elements (N*BITS/8 bytes) at byte offset off of a
+// peer's tile, in the low bits.
+template <int BITS, int N>
 __device__ __forceinline__ u32x2 load_codes_at(__amdgpu_buffer_rsrc_t tile, uint32_t off) {
-    if constexpr (BITS == 2) return u32x2{(uint32_t)__builtin_amdgcn_raw_buffer_load_b16(tile, off, 0, kLoadNt), 0u};
-    else if constexpr (BITS == 4) return u32x2{__builtin_amdgcn_raw_buffer_load_b32(tile, off, 0, kLoadNt), 0u};
+    constexpr int NB = N * BITS / 8;
+    if constexpr (NB == 1) return u32x2{(uint32_t)__builtin_amdgcn_raw_buffer_load_b8(tile, off, 0, kLoadNt), 0u};
+    else if constexpr (NB == 2) return u32x2{(uint32_t)__builtin_amdgcn_raw_buffer_load_b16(tile, off, 0, kLoadNt), 0u};
+    else if constexpr (NB == 4) return u32x2{__builtin_amdgcn_raw_buffer_load_b32(tile, off, 0, kLoadNt), 0u};
     else return __builtin_amdgcn_raw_buffer_load_b64(tile, off, 0, kLoadNt);
 }
 
@@ -59,35 +63,51 @@ __device__ __forceinline__ void acc_byte(float& a, uint32_t x, float step, float
 // exact value is q*step, rounded once, so the result is bit-identical to rounding q*step
 // (2^(b-1)*step is exact).  2-bit codes use a sign-extending bit-field extract.
 // off is -2^(b-1)*step, computed by the caller (once per scale, not per 8 codes).
+// Codes 0-3 use the scale (sa, oa) and codes 4-7 (sb, ob): the lane's two pieces may sit
+// in different scale blocks.
 template <int BITS>
-__device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float step, float off) {
+__device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float sa, float oa, float sb, float ob) {
     if constexpr (BITS == 4) {
         const uint32_t x = w.x ^ 0x88888888u;
         const uint32_t lo = x & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
         const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-        acc_byte<0>(acc[0], lo, step, off);
-        acc_byte<0>(acc[1], hi, step, off);
-        acc_byte<1>(acc[2], lo, step, off);
-        acc_byte<1>(acc[3], hi, step, off);
-        acc_byte<2>(acc[4], lo, step, off);
-        acc_byte<2>(acc[5], hi, step, off);
-        acc_byte<3>(acc[6], lo, step, off);
-        acc_byte<3>(acc[7], hi, step, off);
+        acc_byte<0>(acc[0], lo, sa, oa);
+        acc_byte<0>(acc[1], hi, sa, oa);
+        acc_byte<1>(acc[2], lo, sa, oa);
+        acc_byte<1>(acc[3], hi, sa, oa);
+        acc_byte<2>(acc[4], lo, sb, ob);
+        acc_byte<2>(acc[5], hi, sb, ob);
+        acc_byte<3>(acc[6], lo, sb, ob);
+        acc_byte<3>(acc[7], hi, sb, ob);
     } else if constexpr (BITS == 8) {
         const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
-        acc_byte<0>(acc[0], x0, step, off);
-        acc_byte<1>(acc[1], x0, step, off);
-        acc_byte<2>(acc[2], x0, step, off);
-        acc_byte<3>(acc[3], x0, step, off);
-        acc_byte<0>(acc[4], x1, step, off);
-        acc_byte<1>(acc[5], x1, step, off);
-        acc_byte<2>(acc[6], x1, step, off);
-        acc_byte<3>(acc[7], x1, step, off);
+        acc_byte<0>(acc[0], x0, sa, oa);
+        acc_byte<1>(acc[1], x0, sa, oa);
+        acc_byte<2>(acc[2], x0, sa, oa);
+        acc_byte<3>(acc[3], x0, sa, oa);
+        acc_byte<0>(acc[4], x1, sb, ob);
+        acc_byte<1>(acc[5], x1, sb, ob);
+        acc_byte<2>(acc[6], x1, sb, ob);
+        acc_byte<3>(acc[7], x1, sb, ob);
     } else {
 #pragma unroll
-        for (int j = 0; j < kDrVec; ++j) acc[j] = acc[j] + (float)code_of<BITS>(w, j) * step;
+        for (int j = 0; j < kDrVec; ++j) acc[j] = acc[j] + (float)code_of<BITS>(w, j) * (j < 4 ? sa : sb);
     }
 }
+
+// Lane layout of a 512-element sub-tile: lane l owns 8 outputs as two pieces of 4
+// consecutive elements.  Split (fp32 output, and the fused Adam step with its fp32
+// weights and moments): the pieces sit at 4l and 256 + 4l, so every load and store
+// instruction of a 4-byte stream covers one contiguous 1 KB run.  Contiguous (bf16
+// output): the lane's 8 outputs are consecutive (a 16-byte store each, already
+// contiguous across the wave).  In the Adam step's traffic twin the split layout with
+// non-temporal state loads and stores streams at 6.0 TB/s, against 5.4 for consecutive
+// elements with plain ones.
+template <int MODE>
+struct DrLayout {
+    static constexpr bool kSplit = MODE != kDrOutBf16;
+    static __device__ __forceinline__ int piece(int l, int pc) { return kSplit ? pc * 256 + l * 4 : l * 8 + pc * 4; }
+};
 
 template <int BITS, int B, bool FIXED>
 __device__ __forceinline__ float peer_step(const DrPeerDev& pe, int64_t i0, float fixed_step) {
@@ -96,8 +116,10 @@ __device__ __forceinline__ float peer_step(const DrPeerDev& pe, int64_t i0, floa
     else return pe.absmax[i0 / B] / (float)QMAX;  // 0 for an all-zero block
 }
 
+// The lane's 8 outputs of a sub-tile, pieces at elements i0 and i1 (i1 = i0 + 4 in the
+// contiguous layout).
 template <int MODE>
-__device__ __forceinline__ void store_out8(void* out, int64_t i0, const float (&acc)[kDrVec], float scale) {
+__device__ __forceinline__ void store_out8(void* out, int64_t i0, int64_t i1, const float (&acc)[kDrVec], float scale) {
     if constexpr (MODE == kDrOutBf16) {
         u32x4 s;
         s.x = bf16x2_rne(acc[0] * scale, acc[1] * scale);
@@ -106,11 +128,10 @@ __device__ __forceinline__ void store_out8(void* out, int64_t i0, const float (&
         s.w = bf16x2_rne(acc[6] * scale, acc[7] * scale);
         __builtin_nontemporal_store(s, (u32x4*)((uint16_t*)out + i0));
     } else {
-        f32x4* o = (f32x4*)((float*)out + i0);
         f32x4 a = {acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale};
         f32x4 b = {acc[4] * scale, acc[5] * scale, acc[6] * scale, acc[7] * scale};
-        __builtin_nontemporal_store(a, o);
-        __builtin_nontemporal_store(b, o + 1);
+        __builtin_nontemporal_store(a, (f32x4*)((float*)out + i0));
+        __builtin_nontemporal_store(b, (f32x4*)((float*)out + i1));
     }
 }
 
@@ -122,29 +143,20 @@ __device__ __forceinline__ void adam1(const DrParams& p, float g, float& th, flo
     th = th - p.lr * (m * u);
 }
 
-#ifndef LOCO_DRA_NT_LOADS
-#define LOCO_DRA_NT_LOADS 0
-#endif
-__device__ __forceinline__ void load8f(const float* src, int64_t i0, float (&x)[kDrVec]) {
-    const f32x4* q = (const f32x4*)(src + i0);
-    const f32x4 a = LOCO_DRA_NT_LOADS ? __builtin_nontemporal_load(q) : q[0];
-    const f32x4 b = LOCO_DRA_NT_LOADS ? __builtin_nontemporal_load(q + 1) : q[1];
+// 4 consecutive fp32 of the optimizer state, non-temporal (read once, written once).
+__device__ __forceinline__ void load4f(const float* src, int64_t i0, float* x) {
+    const f32x4 a = __builtin_nontemporal_load((const f32x4*)(src + i0));
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-// Plain stores: the optimizer state was just read through the caches, and non-temporal
-// stores of its half-lines (each store instruction of a wave writes 16 of every 32 bytes)
-// reached HBM as ~5% extra write bytes, varying from call to call; plain stores write
-// exactly the state's bytes in the same time.
-__device__ __forceinline__ void store8f(float* dst, int64_t i0, const float (&x)[kDrVec]) {
-    f32x4* q = (f32x4*)(dst + i0);
-    q[0] = f32x4{x[0], x[1], x[2], x[3]};
-    q[1] = f32x4{x[4], x[5], x[6], x[7]};
+__device__ __forceinline__ void store4f(float* dst, int64_t i0, const float* x) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, (f32x4*)(dst + i0));
 }
 
 template <int BITS, int B, bool FIXED, int MODE>
 __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
+    using LY = DrLayout<MODE>;
+    constexpr bool SPLIT = LY::kSplit;
     constexpr int U = dr_unroll(MODE);
     constexpr int TILE = dr_tile_elems(MODE);
     constexpr bool ADAM = MODE == kDrOutAdam;
@@ -153,55 +165,71 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
     const int lane = lane_id();
     const int64_t nwaves = (int64_t)gridDim.x * (kDrThreads / kWave);
     const int64_t wg = xcd_remap<kXcds, kDrXcdRun>(blockIdx.x, gridDim.x);
+    // element offsets, within the tile, of the lane's pieces in each sub-tile
+    int pos[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) pos[u][pc] = u * SUB + LY::piece(lane, pc);
     for (int64_t t = wg * (kDrThreads / kWave) + uniform(threadIdx.x / kWave); t < p.ntiles;
          t += nwaves) {
-        const int64_t base = t * TILE + lane * kDrVec;
+        const int64_t tb = t * TILE;  // the tile's first element
         float acc[U][kDrVec];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < kDrVec; ++j) acc[u][j] = 0.0f;
 
-        if ((t + 1) * TILE <= p.n) {
+        if (tb + TILE <= p.n) {
             // The optimizer state is loaded first, so its latency overlaps the payloads'.
             float th[ADAM ? U : 1][kDrVec], mo[ADAM ? U : 1][kDrVec], ve[ADAM ? U : 1][kDrVec];
             if constexpr (ADAM) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    load8f(p.theta, base + u * SUB, th[u]);
-                    load8f(p.m, base + u * SUB, mo[u]);
-                    load8f(p.v, base + u * SUB, ve[u]);
-                }
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int pc = 0; pc < 2; ++pc) {
+                        load4f(p.theta, tb + pos[u][pc], th[u] + 4 * pc);
+                        load4f(p.m, tb + pos[u][pc], mo[u] + 4 * pc);
+                        load4f(p.v, tb + pos[u][pc], ve[u] + 4 * pc);
+                    }
             }
             // whole wave tile in range.  The tile spans BPT scale blocks; the steps of G
             // peers x BPT blocks are computed one per lane (lane l divides peer l / BPT's
             // block l % BPT: one division per lane per G peers) and each lane fetches its
-            // block's step with ds_bpermute.  Every payload load goes through a buffer
+            // pieces' steps with ds_bpermute.  Every payload load goes through a buffer
             // resource over the peer's part of the tile (its base in SGPRs, a 32-bit lane
             // offset).
             constexpr int BPT = TILE / B;
             constexpr int G = 64 / BPT;
-            constexpr int CB = kDrVec * BITS / 8;  // code bytes per lane per sub-tile
+            // the two pieces of a lane lie in different blocks (split layout, blocks of at
+            // most 256 elements)
+            constexpr bool TWO = SPLIT && B <= SUB / 2;
             const int64_t blk0 = t * (TILE / B);
             const int64_t cbase = t * (int64_t)(TILE * BITS / 8);
-            const uint32_t coff = (uint32_t)lane * CB;
             const uint32_t aoff = (uint32_t)(lane % BPT) * 4u;
             const int myq = lane / BPT;
-            int myblk[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) myblk[u] = (int)((base + u * SUB) / B - blk0);
             for (int pg = 0; pg < p.npeers; pg += G) {
                 const int ng = p.npeers - pg < G ? p.npeers - pg : G;
                 // codes of a batch of peers, all loads in flight together (slots past the
                 // group read later peers or the table's copies of the last one, and are
-                // not accumulated)
+                // not accumulated).  Split: a piece's 4 codes per load, merged so that
+                // codes 0-3 are piece 0's and 4-7 piece 1's.
                 u32x2 w[kDrPeerBatch][U];
                 auto load_batch = [&](int q0) {
 #pragma unroll
                     for (int b = 0; b < kDrPeerBatch; ++b) {
                         const auto ct = buffer_rsrc(p.peer[pg + q0 + b].codes + cbase, TILE * BITS / 8);
 #pragma unroll
-                        for (int u = 0; u < U; ++u) w[b][u] = load_codes_at<BITS>(ct, coff + u * (SUB * BITS / 8));
+                        for (int u = 0; u < U; ++u) {
+                            if constexpr (SPLIT) {
+                                const u32x2 c0 = load_codes_at<BITS, 4>(ct, (uint32_t)pos[u][0] * BITS / 8);
+                                const u32x2 c1 = load_codes_at<BITS, 4>(ct, (uint32_t)pos[u][1] * BITS / 8);
+                                if constexpr (BITS == 8) w[b][u] = u32x2{c0.x, c1.x};
+                                else w[b][u] = u32x2{c0.x | (c1.x << (4 * BITS)), 0u};
+                            } else {
+                                w[b][u] = load_codes_at<BITS, 8>(ct, (uint32_t)pos[u][0] * BITS / 8);
+                            }
+                        }
                     }
                 };
                 load_batch(0);  // issued before the scales, so both latencies overlap
@@ -226,28 +254,40 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                 const float offp = -(float)(1 << (BITS - 1)) * stp;
                 for (int q0 = 0; q0 < ng; q0 += kDrPeerBatch) {
                     if (q0 > 0) load_batch(q0);
-                    // byte address (ds_bpermute) of the lane holding peer q0's scale of this
-                    // lane's block in sub-tile u; peer q0 + b is b*BPT lanes further, an
+                    // byte address (ds_bpermute) of the lane holding peer q0's scale of a
+                    // piece's block in sub-tile u; peer q0 + b is b*BPT lanes further, an
                     // immediate offset
-                    int src[U];
+                    int src[U][2];
 #pragma unroll
-                    for (int u = 0; u < U; ++u) src[u] = (q0 * BPT + myblk[u]) * 4;
+                    for (int u = 0; u < U; ++u)
+#pragma unroll
+                        for (int pc = 0; pc < 2; ++pc) src[u][pc] = (q0 * BPT + pos[u][pc] / B) * 4;
                     // accumulate in peer order
 #pragma unroll
                     for (int b = 0; b < kDrPeerBatch; ++b) {
                         if (q0 + b < ng) {
 #pragma unroll
                             for (int u = 0; u < U; ++u) {
-                                float step = stp, off = offp;
+                                float sa = stp, oa = offp, sb = stp, ob = offp;
                                 if constexpr (!FIXED) {
-                                    const int a = src[u] + b * BPT * 4;
-                                    step = __builtin_bit_cast(
-                                        float, __builtin_amdgcn_ds_bpermute(a, __builtin_bit_cast(int, stp)));
+                                    const int a0 = src[u][0] + b * BPT * 4;
+                                    sa = __builtin_bit_cast(
+                                        float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, stp)));
                                     if constexpr (BITS != 2)
-                                        off = __builtin_bit_cast(
-                                            float, __builtin_amdgcn_ds_bpermute(a, __builtin_bit_cast(int, offp)));
+                                        oa = __builtin_bit_cast(
+                                            float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, offp)));
+                                    sb = sa;
+                                    ob = oa;
+                                    if constexpr (TWO) {
+                                        const int a1 = src[u][1] + b * BPT * 4;
+                                        sb = __builtin_bit_cast(
+                                            float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, stp)));
+                                        if constexpr (BITS != 2)
+                                            ob = __builtin_bit_cast(
+                                                float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, offp)));
+                                    }
                                 }
-                                accumulate8<BITS>(acc[u], w[b][u], step, off);
+                                accumulate8<BITS>(acc[u], w[b][u], sa, oa, sb, ob);
                             }
                         }
                     }
@@ -258,59 +298,64 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int j = 0; j < kDrVec; ++j) adam1(p, acc[u][j] * p.out_scale, th[u][j], mo[u][j], ve[u][j]);
-                    store8f(p.theta, base + u * SUB, th[u]);
-                    store8f(p.m, base + u * SUB, mo[u]);
-                    store8f(p.v, base + u * SUB, ve[u]);
-                    if (p.theta_bf16) {
-                        u32x4 s;
-                        s.x = bf16x2_rne(th[u][0], th[u][1]);
-                        s.y = bf16x2_rne(th[u][2], th[u][3]);
-                        s.z = bf16x2_rne(th[u][4], th[u][5]);
-                        s.w = bf16x2_rne(th[u][6], th[u][7]);
-                        *(u32x4*)(p.theta_bf16 + base + u * SUB) = s;
+#pragma unroll
+                    for (int pc = 0; pc < 2; ++pc) {
+                        const int64_t i0 = tb + pos[u][pc];
+                        store4f(p.theta, i0, th[u] + 4 * pc);
+                        store4f(p.m, i0, mo[u] + 4 * pc);
+                        store4f(p.v, i0, ve[u] + 4 * pc);
+                        if (p.theta_bf16) {
+                            const u32x2 s = {bf16x2_rne(th[u][4 * pc], th[u][4 * pc + 1]),
+                                             bf16x2_rne(th[u][4 * pc + 2], th[u][4 * pc + 3])};
+                            __builtin_nontemporal_store(s, (u32x2*)(p.theta_bf16 + i0));
+                        }
                     }
                 }
             } else {
 #pragma unroll
-                for (int u = 0; u < U; ++u) store_out8<MODE>(p.out, base + u * SUB, acc[u], p.out_scale);
+                for (int u = 0; u < U; ++u) store_out8<MODE>(p.out, tb + pos[u][0], tb + pos[u][1], acc[u], p.out_scale);
             }
         } else {
             // ragged tail: element-wise, reading only the bytes that exist
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i0 = base + u * SUB;
-                const int64_t left = p.n - i0;
-                const int nvalid = left <= 0 ? 0 : (left >= kDrVec ? kDrVec : (int)left);
-                if (nvalid == 0) continue;
-                for (int pi = 0; pi < p.npeers; ++pi) {
-                    const DrPeerDev pe = p.peer[pi];
-                    const float step = peer_step<BITS, B, FIXED>(pe, i0, p.fixed_step);
 #pragma unroll
-                    for (int j = 0; j < kDrVec; ++j) {
-                        if (j < nvalid) {
-                            const int64_t i = i0 + j;
-                            const uint32_t byte = pe.codes[(i * BITS) / 8];
-                            const int q = __builtin_amdgcn_sbfe(byte, (int)((i * BITS) % 8), BITS);
-                            acc[u][j] = acc[u][j] + (float)q * step;
+                for (int pc = 0; pc < 2; ++pc) {
+                    const int64_t i0 = tb + pos[u][pc];
+                    const int64_t left = p.n - i0;
+                    const int nvalid = left <= 0 ? 0 : (left >= 4 ? 4 : (int)left);
+                    if (nvalid == 0) continue;
+                    float* ac = acc[u] + 4 * pc;
+                    for (int pi = 0; pi < p.npeers; ++pi) {
+                        const DrPeerDev pe = p.peer[pi];
+                        const float step = peer_step<BITS, B, FIXED>(pe, i0, p.fixed_step);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            if (j < nvalid) {
+                                const int64_t i = i0 + j;
+                                const uint32_t byte = pe.codes[(i * BITS) / 8];
+                                const int q = __builtin_amdgcn_sbfe(byte, (int)((i * BITS) % 8), BITS);
+                                ac[j] = ac[j] + (float)q * step;
+                            }
                         }
                     }
-                }
 #pragma unroll
-                for (int j = 0; j < kDrVec; ++j) {
-                    if (j < nvalid) {
-                        const float g = acc[u][j] * p.out_scale;
-                        if constexpr (ADAM) {
+                    for (int j = 0; j < 4; ++j) {
+                        if (j < nvalid) {
                             const int64_t i = i0 + j;
-                            float th1 = p.theta[i], m1 = p.m[i], v1 = p.v[i];
-                            adam1(p, g, th1, m1, v1);
-                            p.theta[i] = th1;
-                            p.m[i] = m1;
-                            p.v[i] = v1;
-                            if (p.theta_bf16) p.theta_bf16[i] = bf16_rne(th1);
-                        } else if constexpr (MODE == kDrOutBf16) {
-                            ((uint16_t*)p.out)[i0 + j] = bf16_rne(g);
-                        } else {
-                            ((float*)p.out)[i0 + j] = g;
+                            const float g = ac[j] * p.out_scale;
+                            if constexpr (ADAM) {
+                                float th1 = p.theta[i], m1 = p.m[i], v1 = p.v[i];
+                                adam1(p, g, th1, m1, v1);
+                                p.theta[i] = th1;
+                                p.m[i] = m1;
+                                p.v[i] = v1;
+                                if (p.theta_bf16) p.theta_bf16[i] = bf16_rne(th1);
+                            } else if constexpr (MODE == kDrOutBf16) {
+                                ((uint16_t*)p.out)[i] = bf16_rne(g);
+                            } else {
+                                ((float*)p.out)[i] = g;
+                            }
                         }
                     }
                 }

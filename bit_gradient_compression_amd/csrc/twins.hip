@@ -106,9 +106,11 @@ __global__ __launch_bounds__(kThreads) void twin_cq_kernel(const void* g, void* 
 }
 
 // ---- dequant-reduce (bf16 / fp32 shard, or the fused Adam step) ----------------------
-// Per lane and sub-tile: every peer's codes of 8 elements (non-temporal) and its block
-// absmax, then 8 outputs (16 B bf16 or 32 B fp32, non-temporal); or, for the Adam step,
-// theta, m and v of 8 elements loaded and stored (plain) and the bf16 weight copy.
+// Per lane and sub-tile, in the kernel's lane layout (8 consecutive outputs for a bf16
+// shard; two pieces of 4 at 4l and 256 + 4l for an fp32 shard and the Adam step): every
+// peer's codes of the lane's elements (non-temporal) and its block absmax, then the 8
+// outputs (non-temporal); or, for the Adam step, theta, m and v loaded and stored and the
+// bf16 weight copy stored (all non-temporal).
 
 struct TwinPeers {
     const uint8_t* codes[kTwinMaxPeers];
@@ -118,22 +120,22 @@ struct TwinPeers {
 template <int BITS, int MODE, int U, int P>
 __global__ __launch_bounds__(kThreads) void twin_dr_kernel(TwinPeers pp, int64_t ntiles, int lb, void* out,
                                                            float* theta, float* m, float* v, uint16_t* tb) {
+    constexpr bool SPLIT = MODE != 1;
     const int lane = lane_id();
     const int64_t wg = xcd_remap<8, 16>(blockIdx.x, gridDim.x);
     const int64_t t = wg * (kThreads / 64) + uniform(threadIdx.x / 64);
     if (t >= ntiles) return;
+    auto at = [&](int u, int pc) { return (t * U + u) * 512 + (SPLIT ? pc * 256 + lane * 4 : lane * 8 + pc * 4); };
     f32x4 th[U][2], mo[U][2], ve[U][2];
     if constexpr (MODE == 2) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i0 = (t * U + u) * 512 + lane * 8;
-            th[u][0] = *(const f32x4*)(theta + i0);
-            th[u][1] = *((const f32x4*)(theta + i0) + 1);
-            mo[u][0] = *(const f32x4*)(m + i0);
-            mo[u][1] = *((const f32x4*)(m + i0) + 1);
-            ve[u][0] = *(const f32x4*)(v + i0);
-            ve[u][1] = *((const f32x4*)(v + i0) + 1);
-        }
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc) {
+                th[u][pc] = __builtin_nontemporal_load((const f32x4*)(theta + at(u, pc)));
+                mo[u][pc] = __builtin_nontemporal_load((const f32x4*)(m + at(u, pc)));
+                ve[u][pc] = __builtin_nontemporal_load((const f32x4*)(v + at(u, pc)));
+            }
     }
     uint32_t acc[U];
 #pragma unroll
@@ -142,40 +144,35 @@ __global__ __launch_bounds__(kThreads) void twin_dr_kernel(TwinPeers pp, int64_t
     for (int p = 0; p < P; ++p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t i0 = (t * U + u) * 512 + lane * 8;
-            const uint8_t* c = pp.codes[p] + (i0 * BITS) / 8;
             uint32_t w;
-            if constexpr (BITS == 8) {
-                const u32x2 x = __builtin_nontemporal_load((const u32x2*)c);
-                w = x.x ^ x.y;
-            } else if constexpr (BITS == 4) {
-                w = __builtin_nontemporal_load((const uint32_t*)c);
+            if constexpr (SPLIT) {
+                w = __builtin_nontemporal_load((const uint16_t*)(pp.codes[p] + at(u, 0) * BITS / 8)) ^
+                    __builtin_nontemporal_load((const uint16_t*)(pp.codes[p] + at(u, 1) * BITS / 8));
             } else {
-                w = __builtin_nontemporal_load((const uint16_t*)c);
+                w = __builtin_nontemporal_load((const uint32_t*)(pp.codes[p] + at(u, 0) * BITS / 8));
             }
-            acc[u] ^= w ^ __float_as_uint(pp.absmax[p][i0 >> lb]);
+            acc[u] ^= w ^ __float_as_uint(pp.absmax[p][at(u, 0) >> lb]);
         }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t i0 = (t * U + u) * 512 + lane * 8;
         const uint32_t a = acc[u] & 0x3F7FFFFFu;
         if constexpr (MODE == 1) {
-            __builtin_nontemporal_store(u32x4{a, a, a, a}, (u32x4*)((uint16_t*)out + i0));
+            __builtin_nontemporal_store(u32x4{a, a, a, a}, (u32x4*)((uint16_t*)out + at(u, 0)));
         } else if constexpr (MODE == 0) {
             const f32x4 x = __builtin_bit_cast(f32x4, u32x4{a, a, a, a});
-            __builtin_nontemporal_store(x, (f32x4*)((float*)out + i0));
-            __builtin_nontemporal_store(x, (f32x4*)((float*)out + i0) + 1);
+            __builtin_nontemporal_store(x, (f32x4*)((float*)out + at(u, 0)));
+            __builtin_nontemporal_store(x, (f32x4*)((float*)out + at(u, 1)));
         } else {
             const float s = __uint_as_float(a);
             const f32x4 d = {s, s, s, s};
-            *(f32x4*)(theta + i0) = th[u][0] + d;
-            *((f32x4*)(theta + i0) + 1) = th[u][1] + d;
-            *(f32x4*)(m + i0) = mo[u][0] + d;
-            *((f32x4*)(m + i0) + 1) = mo[u][1] + d;
-            *(f32x4*)(v + i0) = ve[u][0] + d;
-            *((f32x4*)(v + i0) + 1) = ve[u][1] + d;
-            if (tb) *(u32x4*)(tb + i0) = u32x4{a, a, a, a};
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc) {
+                __builtin_nontemporal_store(th[u][pc] + d, (f32x4*)(theta + at(u, pc)));
+                __builtin_nontemporal_store(mo[u][pc] + d, (f32x4*)(m + at(u, pc)));
+                __builtin_nontemporal_store(ve[u][pc] + d, (f32x4*)(v + at(u, pc)));
+                if (tb) __builtin_nontemporal_store(u32x2{a, a}, (u32x2*)(tb + at(u, pc)));
+            }
         }
     }
 }
