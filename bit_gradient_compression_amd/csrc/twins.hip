@@ -179,9 +179,9 @@ __global__ __launch_bounds__(kThreads) void twin_dr_kernel(TwinPeers pp, int64_t
 
 // ---- Top-k ---------------------------------------------------------------------------
 // One 256-thread workgroup per 4096-element chunk: thread t loads rows q*1024 + 4t of the
-// gradient (non-temporal) and the error (plain) as 16-byte vectors and stores the error
-// rows back (plain); the first k threads store an index, the first ceil(k*bits/8) a code
-// byte, thread 0 the chunk's absmax.
+// gradient and the error as 16-byte vectors and stores the error rows back (all
+// non-temporal); the first k threads store an index, the first ceil(k*bits/8) a code byte,
+// thread 0 the chunk's absmax.
 
 __global__ __launch_bounds__(kThreads) void twin_tk_kernel(const float* g, float* e, uint16_t* idx, uint8_t* codes,
                                                            float* absmax, int64_t nchunks, int k, int nbytes) {
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void twin_tk_kernel(const float* g, float
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         gv[q] = __builtin_nontemporal_load((const u32x4*)(gb + q * 1024 + tid * 4));
-        ev[q] = *(const u32x4*)(eb + q * 1024 + tid * 4);
+        ev[q] = __builtin_nontemporal_load((const u32x4*)(eb + q * 1024 + tid * 4));
     }
     uint32_t x = 0;
 #pragma unroll
