@@ -15,15 +15,21 @@ compensate-quantize then dequant-reduce of 4 peers), which fits in the Infinity 
 is bound by launch latency: its time per step is reported eagerly and as replays of a HIP
 graph, with no roofline claim.
 
-Each mode is timed back to back and again with a 1 GiB read before each launch (which
-keeps its inputs out of the Infinity Cache and keeps other launches' dirty lines out of
-its time); its GB/s use the slower of the two.
+Every kernel (the step's two and each mode) is timed back to back and again with a 1 GiB
+read before each launch (which keeps its inputs out of the Infinity Cache and keeps other
+launches' dirty lines out of its time), with median, p10 and p90; its GB/s use the slower
+of the two averages.  Beside each kernel its traffic twin (libloco_twins.so: the same
+loads and stores in the same launch shape, no compression arithmetic) is timed the same
+way: frac_twin = twin time / kernel time is how close the kernel runs to the ceiling of
+its own stream mix.
 
 Prints one JSON line.  value = gradient GB/s = 842,000,000 x 2 bytes / step time.
-roofline: the compensate-quantize kernel's algorithmic bytes / its average launch time
-(HIP events on its stream) against 8 TB/s.  copy_ceiling: a plain 1 GiB streaming copy
-for context; every kernel also reports its GB/s over it (frac_copy).  cpu_baseline: the
-CPU oracle on a bounded sample of the same workload on this host, in one process, and
+roofline: the compensate-quantize kernel's algorithmic bytes / its launch time against
+8 TB/s, the launch time being the slowest of its average inside the timed steps (HIP
+events on its stream) and its back-to-back and cache-flushed averages.  copy_ceiling: a
+hand-written streaming copy (one 16-byte vector per thread, 1 GiB in, 1 GiB out) for
+context; every kernel also reports its GB/s over it (frac_copy).  cpu_baseline: the CPU
+oracle on a bounded sample of the same workload on this host, in one process, and
 (parallel) fanned out over the host's cores.
 """
 
@@ -265,7 +271,9 @@ def main():
     if not os.path.exists(B.LIB_PATH):
         B.build()
     from bit_gradient_compression_amd import loco
+    from bit_gradient_compression_amd import twins
     loco.load()
+    twins.load()
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -295,19 +303,17 @@ def main():
     out = torch.empty(part, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    # a plain 1 GiB device copy (its launches calibrate the HBM byte counters), then the
-    # streaming ceiling for context: a 1 GiB read + 1 GiB write through torch's elementwise
-    # kernel (neg into a second buffer), which streams faster than copy_'s blit kernel
+    # the streaming ceiling for context: a hand-written copy of 1 GiB into 1 GiB (one 16-byte
+    # vector per thread, non-temporal); its launches also calibrate the HBM byte counters
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
-        torch.neg(src, out=dst)
+        twins.copy(src, dst)
     torch.cuda.synchronize()
     cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
     for a, b in cevs:
         a.record(stream)
-        torch.neg(src, out=dst)
+        twins.copy(src, dst)
         b.record(stream)
     torch.cuda.synchronize()
     copy_ms = sorted(a.elapsed_time(b) for a, b in cevs)[len(cevs) // 2]
@@ -342,19 +348,41 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     cq_alg = cq_bytes(sizes, 2, 4, BITS, BLOCK)
     dr_alg = dr_bytes(part, PARTS, BITS, BLOCK, 2)
-    cq_avg_s = avg(cq_ms) / 1e3
-    dr_avg_s = avg(dr_ms) / 1e3
-    achieved = cq_alg / cq_avg_s / 1e9
+    reps = max(10, args.steps // 2)
+    # the same two kernels by the modes' protocol (back to back, and cache-flushed), then
+    # their traffic twins on the same buffers (the twins overwrite the error buffer and
+    # the shard, which nothing reads afterwards)
+    cq_call = lambda: loco.loco_compensate_quantize(segs, bits=BITS, block=BLOCK, beta=BETA, stream=stream)  # noqa: E731
+    dr_call = lambda: loco.loco_dequant_reduce(payloads, part, bits=BITS, block=BLOCK, out=out,  # noqa: E731
+                                               out_scale=1.0 / PARTS, stream=stream)
+    cq_prot = timed(cq_call, stream, reps)
+    cq_timing = spread()
+    dr_prot = timed(dr_call, stream, reps)
+    dr_timing = spread()
+    # the roofline takes the slowest of the in-step average and the two protocol averages
+    cq_time_ms = max(avg(cq_ms), cq_prot)
+    cq_source = "timed steps" if cq_time_ms == avg(cq_ms) else "protocol"
+    achieved = cq_alg / (cq_time_ms / 1e3) / 1e9
+    dr_time_ms = max(avg(dr_ms), dr_prot)
+    codes_cat = torch.empty(n * BITS // 8, dtype=torch.uint8, device=dev)
+    absmax_cat = torch.empty(-(-n // BLOCK), dtype=torch.float32, device=dev)
+    cq_twin = twin_of(lambda: twins.cq(g, e, codes_cat, absmax_cat, bits=BITS, block=BLOCK), stream, reps, cq_alg,
+                      cq_time_ms)
+    del codes_cat, absmax_cat
+    dr_twin = twin_of(lambda: twins.dr(payloads, part, bits=BITS, block=BLOCK, out=out), stream, reps, dr_alg,
+                      dr_time_ms)
 
     kernels = {
-        "compensate_quantize_4bit": {"avg_ms": round(avg(cq_ms), 4), "p10_ms": round(cq_ms[len(cq_ms) // 10], 4),
-                                     "p90_ms": round(cq_ms[(len(cq_ms) * 9) // 10], 4), "alg_bytes": cq_alg,
-                                     "GBps": round(achieved, 1), "frac_hbm": round(achieved / HBM_PEAK_GBPS, 4)},
-        "dequant_reduce_8peers": {"avg_ms": round(avg(dr_ms), 4), "alg_bytes": dr_alg,
-                                  "GBps": round(dr_alg / dr_avg_s / 1e9, 1),
-                                  "frac_hbm": round(dr_alg / dr_avg_s / 1e9 / HBM_PEAK_GBPS, 4)},
+        "compensate_quantize_4bit": {"avg_ms_timed_steps": round(avg(cq_ms), 4),
+                                     "p10_ms_timed_steps": round(cq_ms[len(cq_ms) // 10], 4),
+                                     "p90_ms_timed_steps": round(cq_ms[(len(cq_ms) * 9) // 10], 4),
+                                     **cq_timing, "ms": round(cq_time_ms, 4), "alg_bytes": cq_alg,
+                                     "GBps": round(achieved, 1), "frac_hbm": round(achieved / HBM_PEAK_GBPS, 4),
+                                     **cq_twin},
+        "dequant_reduce_8peers": {"avg_ms_timed_steps": round(avg(dr_ms), 4), **dr_timing, "ms": round(dr_time_ms, 4),
+                                  "alg_bytes": dr_alg, "GBps": round(dr_alg / dr_time_ms / 1e6, 1),
+                                  "frac_hbm": round(dr_alg / dr_time_ms / 1e6 / HBM_PEAK_GBPS, 4), **dr_twin},
     }
-
     measured = load_traffic()
     traffic = measured.get("compensate_quantize_4bit", {}).get("hbm_bytes")
     for k, v in measured.items():
@@ -371,12 +399,17 @@ def main():
         segs8 = [(g[i * part:(i + 1) * part], e8[i * part:(i + 1) * part], codes8[i], absmax[i])
                  for i in range(PARTS)]
         ms = timed(lambda: loco.loco_compensate_quantize(segs8, bits=8, block=BLOCK, beta=BETA, stream=stream),
-                   stream, max(10, args.steps // 2))
+                   stream, reps)
         b8 = cq_bytes(sizes, 2, 4, 8, BLOCK)
         modes["compensate_quantize_8bit_7b_shard"] = {"avg_ms": round(ms, 4), **spread(), "alg_bytes": b8,
                                                       "GBps": round(b8 / ms / 1e6, 1),
                                                       "frac_hbm": round(b8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                                       "grad_GBps": round(n * 2 / ms / 1e6, 1)}
+        c8 = torch.empty(n, dtype=torch.uint8, device=dev)
+        a8 = torch.empty(-(-n // BLOCK), dtype=torch.float32, device=dev)
+        modes["compensate_quantize_8bit_7b_shard"].update(
+            twin_of(lambda: twins.cq(g, e8, c8, a8, bits=8, block=BLOCK), stream, reps, b8, ms))
+        del c8, a8
         jobs.append(("compensate_quantize_8bit_7b_shard", _cq_job(_host_bf16(g[:SAMPLE]), "f32", 8, BLOCK),
                      cq_bytes([SAMPLE], 2, 4, 8, BLOCK), f"the shard's first {SAMPLE:,} elements, one step"))
         del codes8, e8, segs8
@@ -386,33 +419,48 @@ def main():
                                     ("moe", lambda: W.moe_grads(0, device=dev), torch.bfloat16)):
             xg = grads_of()
             xs = [t.numel() for t in xg]
+            sample_host = _host_bf16(xg[0].reshape(-1)[:SAMPLE])
             xsegs = [(t, torch.zeros(m, dtype=edt, device=dev), torch.empty((m * 4 + 7) // 8, dtype=torch.uint8,
                       device=dev), torch.empty(-(-m // 128), device=dev)) for t, m in zip(xg, xs)]
             ms = timed(lambda: loco.loco_compensate_quantize(xsegs, bits=4, block=128, beta=BETA, stream=stream),
-                       stream, max(10, args.steps // 2))
+                       stream, reps)
             bx = cq_bytes(xs, 2, 2 if edt == torch.bfloat16 else 4, 4, 128)
             modes[f"compensate_quantize_4bit_{name}"] = {
                 "workload": f"{sum(xs):,} bf16 in {len(xs)} segments, {'bf16' if edt == torch.bfloat16 else 'fp32'} "
                             "error, 4-bit, block 128",
                 "avg_ms": round(ms, 4), **spread(), "alg_bytes": bx, "GBps": round(bx / ms / 1e6, 1),
                 "frac_hbm": round(bx / ms / 1e6 / HBM_PEAK_GBPS, 4), "grad_GBps": round(sum(xs) * 2 / ms / 1e6, 1)}
+            # the twin streams the same bytes as one segment (scratch buffers of the total size)
+            del xsegs
+            tg = torch.cat([t.reshape(-1) for t in xg])
+            del xg
+            te = torch.zeros(tg.numel(), dtype=edt, device=dev)
+            tc = torch.empty(tg.numel() // 2, dtype=torch.uint8, device=dev)
+            ta = torch.empty(-(-tg.numel() // 128), dtype=torch.float32, device=dev)
+            modes[f"compensate_quantize_4bit_{name}"].update(
+                twin_of(lambda: twins.cq(tg, te, tc, ta, bits=4, block=128), stream, reps, bx, ms))
+            del tg, te, tc, ta
             xe = "bf16" if edt == torch.bfloat16 else "f32"
-            jobs.append((f"compensate_quantize_4bit_{name}", _cq_job(_host_bf16(xg[0].reshape(-1)[:SAMPLE]), xe, 4, 128),
+            jobs.append((f"compensate_quantize_4bit_{name}", _cq_job(sample_host, xe, 4, 128),
                          cq_bytes([SAMPLE], 2, 2 if xe == "bf16" else 4, 4, 128),
                          f"the first tensor's first {SAMPLE:,} elements, one step"))
-            del xg, xsegs
         # the paper's 8-bit error (LoCo Eqn. (7), s_e = 2^17) with 4-bit codes, same shard
         ei8 = torch.zeros(n, dtype=torch.int8, device=dev)
         segs_i8 = [(g[i * part:(i + 1) * part], ei8[i * part:(i + 1) * part], *segs[i][2:]) for i in range(PARTS)]
         ms = timed(lambda: loco.loco_compensate_quantize_ex(segs_i8, bits=BITS, block=BLOCK, beta=BETA,
                                                             err_scale=2.0 ** 17, stream=stream),
-                   stream, max(10, args.steps // 2))
+                   stream, reps)
         bi8 = cq_bytes(sizes, 2, 1, BITS, BLOCK)
         modes["compensate_quantize_4bit_i8err_7b_shard"] = {"avg_ms": round(ms, 4), **spread(), "alg_bytes": bi8,
                                                             "GBps": round(bi8 / ms / 1e6, 1),
                                                             "frac_hbm": round(bi8 / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                                             "grad_GBps": round(n * 2 / ms / 1e6, 1),
                                                             "err_scale": 2.0 ** 17}
+        ci = torch.empty(n * BITS // 8, dtype=torch.uint8, device=dev)
+        ai = torch.empty(-(-n // BLOCK), dtype=torch.float32, device=dev)
+        modes["compensate_quantize_4bit_i8err_7b_shard"].update(
+            twin_of(lambda: twins.cq(g, ei8, ci, ai, bits=BITS, block=BLOCK), stream, reps, bi8, ms))
+        del ci, ai
         jobs.append(("compensate_quantize_4bit_i8err_7b_shard", _cq_job(_host_bf16(g[:SAMPLE]), "i8", BITS, BLOCK),
                      cq_bytes([SAMPLE], 2, 1, BITS, BLOCK), f"the shard's first {SAMPLE:,} elements, one step"))
         del ei8, segs_i8
@@ -425,7 +473,7 @@ def main():
         ms = timed(lambda: loco.loco_dequant_reduce_adam(payloads, part, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS,
                                                          param=th, m=m_, v=v_, lr=1e-4, beta1=0.1, beta2=0.01,
                                                          delta=1e-8, param_bf16=tb, stream=stream),
-                   stream, max(10, args.steps // 2))
+                   stream, reps)
         bda = dr_bytes(part, PARTS, BITS, BLOCK, 0) + 26 * part
         modes["dequant_reduce_adam_8peers"] = {"workload": f"8 peer 4-bit payloads of {part:,} averaged into one "
                                                            "Adam step (fp32 weights, m, v; bf16 weight copy)",
@@ -433,8 +481,11 @@ def main():
                                                "GBps": round(bda / ms / 1e6, 1),
                                                "frac_hbm": round(bda / ms / 1e6 / HBM_PEAK_GBPS, 4)}
         ns = SAMPLE // 4
+        th_h = th[:ns].cpu().numpy()  # before the twin overwrites the weights
+        modes["dequant_reduce_adam_8peers"].update(
+            twin_of(lambda: twins.dr(payloads, part, bits=BITS, block=BLOCK, theta=th, m=m_, v=v_, theta_bf16=tb),
+                    stream, reps, bda, ms))
         spl = [(c[:ns * BITS // 8].cpu().numpy(), a[:ns // BLOCK].cpu().numpy()) for c, a in payloads]
-        th_h = th[:ns].cpu().numpy()
         jobs.append(("dequant_reduce_adam_8peers",
                      lambda spl=spl, th_h=th_h, ns=ns: oracle_module().dequant_reduce_adam(
                          spl, ns, bits=BITS, block=BLOCK, out_scale=1.0 / PARTS, theta=th_h,
@@ -452,7 +503,7 @@ def main():
         tabs = torch.empty(chunks, dtype=torch.float32, device=dev)
         ms = timed(lambda: loco.loco_topk_quantize(gt, et, chunk=TK_CHUNK, k=TK_K, idx=idx, codes=tcodes,
                                                    absmax=tabs, bits=2, ef_decay=1.0, stream=stream),
-                   stream, max(10, args.steps // 2))
+                   stream, reps)
         bt = tk_bytes(nt, TK_CHUNK, TK_K, 2)
         modes["sparseloco_topk_2bit"] = {"workload": f"{nt:,} fp32 N(0,1e-3) + 0.1% +-0.1 outliers, chunk 4096, "
                                                      f"k=82, 2-bit, fp32 error feedback",
@@ -461,6 +512,8 @@ def main():
                                          "grad_GBps": round(nt * 4 / ms / 1e6, 1)}
         nts = 1024 * TK_CHUNK
         gts = gt[:nts].cpu().numpy()
+        modes["sparseloco_topk_2bit"].update(
+            twin_of(lambda: twins.tk(gt, et, idx, tcodes, tabs, k=TK_K, bits=2), stream, reps, bt, ms))
         jobs.append(("sparseloco_topk_2bit",
                      lambda gts=gts: oracle_module().topk_quantize(gts, np.zeros(gts.size, np.float32), chunk=TK_CHUNK,
                                                                   k=TK_K, bits=2, decay=1.0),
@@ -471,13 +524,15 @@ def main():
         sout = torch.empty(nt, dtype=torch.float32, device=dev)
         ms = timed(lambda: loco.loco_sparse_aggregate(spays, nt, chunk=TK_CHUNK, k=TK_K, bits=2, out=sout,
                                                       out_scale=1.0 / PARTS, stream=stream),
-                   stream, max(10, args.steps // 2))
+                   stream, reps)
         bs = sa_bytes(nt, PARTS, TK_CHUNK, TK_K, 2, 4)
         modes["sparseloco_aggregate_8peers"] = {"workload": f"8 peers' Top-k payloads of {nt:,} (chunk 4096, k=82, "
                                                             f"2-bit) into fp32 x 1/8",
                                                 "avg_ms": round(ms, 4), **spread(), "alg_bytes": bs,
                                                 "GBps": round(bs / ms / 1e6, 1),
                                                 "frac_hbm": round(bs / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        modes["sparseloco_aggregate_8peers"].update(
+            twin_of(lambda: twins.sa(spays, nt, k=TK_K, bits=2, out=sout), stream, reps, bs, ms))
         cb2, sch = (TK_K * 2 + 7) // 8, 8192
         sps = [(ix[:sch * TK_K].cpu().numpy().view(np.uint16), c[:sch * cb2].cpu().numpy(), a[:sch].cpu().numpy())
                for ix, c, a in spays]
@@ -577,11 +632,14 @@ def main():
                    "peer_elems": part},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "compensate_quantize_4bit", "alg_bytes_per_launch": cq_alg},
+                     "kernel": "compensate_quantize_4bit", "alg_bytes_per_launch": cq_alg,
+                     "launch_ms": round(cq_time_ms, 4), "launch_ms_from": cq_source,
+                     "frac_twin": kernels["compensate_quantize_4bit"]["frac_twin"]},
         "cpu_baseline": cpu,
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "frac_hbm": round(copy_gbps / HBM_PEAK_GBPS, 4),
-                         "what": "1 GiB read + 1 GiB write streamed by torch.neg(src, out=dst), bytes / median "
-                                 "time of 10; each kernel's frac_copy is its GB/s over this"},
+                         "what": "1 GiB read + 1 GiB write by a hand-written streaming copy (libloco_twins.so, one "
+                                 "16-byte vector per thread), bytes / median time of 10; each kernel's frac_copy is "
+                                 "its GB/s over this"},
         "kernels": kernels,
         "modes": modes,
         "pct_hbm_peak_step": round(100 * (cq_alg + dr_alg) / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
@@ -623,6 +681,14 @@ def timed(fn, stream, reps):
         res[mode] = sorted(a.elapsed_time(b) for a, b in evs)
     timed.last = res
     return max(sum(v) / reps for v in res.values())
+
+
+def twin_of(fn, stream, reps, alg, kernel_ms):
+    """Time a traffic twin by the same protocol as its kernel (the slower of back-to-back and
+    cache-flushed averages) and relate the kernel to it: frac_twin = twin time / kernel time."""
+    ms = timed(fn, stream, reps)
+    return {"twin": {"ms": round(ms, 4), "GBps": round(alg / ms / 1e6, 1), **spread()},
+            "frac_twin": round(ms / kernel_ms, 4)}
 
 
 def spread():
