@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kCqThreads) void cq_kernel(CqParams p) {
     const int lane = lane_id();
     const int64_t nwaves = (int64_t)gridDim.x * (kCqThreads / kWave);
     constexpr int TILE = cq_tile_elems(EK);
-    const int64_t wg = xcd_remap<kXcds, EK == kI8 ? kCqXcdRunI8 : kCqXcdRun>(blockIdx.x, gridDim.x);
+    const int64_t wg = xcd_remap<kXcds, cq_xcd_run(EK)>(blockIdx.x, gridDim.x);
     for (int64_t t = wg * (kCqThreads / kWave) + uniform(threadIdx.x / kWave); t < p.ntiles;
          t += nwaves) {
         const CqSegDev sg = p.seg[find_segment(p, t)];

@@ -25,6 +25,15 @@ namespace loco {
 #ifndef LOCO_CQ_XCD_RUN_I8
 #define LOCO_CQ_XCD_RUN_I8 64
 #endif
+// A bf16 error (6.5 B per element) keeps 1 sub-tile per wave (40 VGPRs) and XCD runs of
+// 32: the MoE experts' 1,409,286,144 elements take 1.46-1.47 ms, against 1.48-1.53 with 2
+// or 4 sub-tiles (runs of 32 or 64) and 1.50-1.52 with runs of 16.
+#ifndef LOCO_CQ_UNROLL_BF16
+#define LOCO_CQ_UNROLL_BF16 1
+#endif
+#ifndef LOCO_CQ_XCD_RUN_BF16
+#define LOCO_CQ_XCD_RUN_BF16 32
+#endif
 #ifndef LOCO_CQ_THREADS
 #define LOCO_CQ_THREADS 256
 #endif
@@ -60,6 +69,10 @@ constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 constexpr int kXcds = 8;
 constexpr int kCqXcdRun = LOCO_CQ_XCD_RUN;
 constexpr int kCqXcdRunI8 = LOCO_CQ_XCD_RUN_I8;
+constexpr int kCqXcdRunBf16 = LOCO_CQ_XCD_RUN_BF16;
+constexpr int cq_xcd_run(int err_kind) {
+    return err_kind == 2 ? kCqXcdRunI8 : err_kind == 1 ? kCqXcdRunBf16 : kCqXcdRun;
+}
 constexpr int kDrXcdRun = LOCO_DR_XCD_RUN;
 constexpr int kSaXcdRun = LOCO_SA_XCD_RUN;
 
@@ -71,7 +84,10 @@ constexpr int kCqUnroll = LOCO_CQ_UNROLL;
 // An int8 error moves 4.5 B per element instead of 10.5, so its waves take more sub-tiles
 // to keep as many bytes in flight.
 constexpr int kCqUnrollI8 = LOCO_CQ_UNROLL_I8;
-constexpr int cq_unroll(int err_kind) { return err_kind == 2 ? kCqUnrollI8 : kCqUnroll; }
+constexpr int kCqUnrollBf16 = LOCO_CQ_UNROLL_BF16;
+constexpr int cq_unroll(int err_kind) {
+    return err_kind == 2 ? kCqUnrollI8 : err_kind == 1 ? kCqUnrollBf16 : kCqUnroll;
+}
 constexpr int cq_tile_elems(int err_kind) { return 64 * kCqVec * cq_unroll(err_kind); }  // per wave tile
 constexpr int kCqThreads = LOCO_CQ_THREADS;
 
