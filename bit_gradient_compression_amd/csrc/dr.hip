@@ -52,22 +52,65 @@ __device__ __forceinline__ int code_of(u32x2 w, int j) {
     else return __builtin_amdgcn_sbfe(w.x, j * BITS, BITS);
 }
 
+// Decoding of 4- and 8-bit codes.  A code is biased to unsigned (c = q + 2^(b-1), one xor
+// for a word of codes) and fl(q*step) is formed as fma(c, step, -2^(b-1)*step): the fma's
+// exact value is q*step, rounded once, so the result is bit-identical to rounding q*step
+// (2^(b-1)*step is exact).  1: c enters the fma as a binary16 subnormal, c * 2^-24, taken
+// straight from the low or high half of a word of masked codes by the mixed-precision fma
+// (v_fma_mix_f32), against a step scaled by 2^24 (exact): per code one masked half-word
+// (two codes per mask), one fma, one add.  0: c is converted with the byte converts
+// (v_cvt_f32_ubyteN), one more instruction per code.
+#ifndef LOCO_DR_DECODE_F16
+#define LOCO_DR_DECODE_F16 1
+#endif
+constexpr bool kDecodeF16 = LOCO_DR_DECODE_F16 != 0;
+constexpr float kF16SubScale = 0x1p24f;  // 2^24: a binary16 subnormal m is m * 2^-24
+
+// The binary16 value of the low / high half of x (m * 2^-24 for m < 1024).
+__device__ __forceinline__ float half_lo(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(x & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(x >> 16));
+}
+
 template <int N>
 __device__ __forceinline__ void acc_byte(float& a, uint32_t x, float step, float off) {
     a = a + __builtin_fmaf(ubyte_to_f32<N>(x), step, off);
 }
 
-// acc[j] += fl(q_j * step) for the 8 codes held in w.  At 4 and 8 bits the codes are
-// biased to unsigned (q + 2^(b-1), one xor for all of them), converted with the byte
-// converts, and fl(q*step) is formed as fma(q + 2^(b-1), step, -2^(b-1)*step): the fma's
-// exact value is q*step, rounded once, so the result is bit-identical to rounding q*step
-// (2^(b-1)*step is exact).  2-bit codes use a sign-extending bit-field extract.
-// off is -2^(b-1)*step, computed by the caller (once per scale, not per 8 codes).
-// Codes 0-3 use the scale (sa, oa) and codes 4-7 (sb, ob): the lane's two pieces may sit
-// in different scale blocks.
+// acc[j] += fl(q_j * step) for the 8 codes held in w: codes 0-3 with the scale (sa, oa),
+// codes 4-7 with (sb, ob) (the lane's two pieces may sit in different scale blocks).
+// w.x holds codes 0-3 in its low and 4-7 in its high 16 bits at 4 bits (2 bits: low and
+// high byte); at 8 bits w.x holds codes 0-3 and w.y codes 4-7.
+// 2 bits: acc + (float)q * step.  4 and 8 bits: s is step * 2^24 (LOCO_DR_DECODE_F16) or
+// step, o = -2^(b-1) * step, with |step| < 2^100 so that neither overflows.
 template <int BITS>
 __device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float sa, float oa, float sb, float ob) {
-    if constexpr (BITS == 4) {
+    if constexpr (BITS == 2) {
+#pragma unroll
+        for (int j = 0; j < kDrVec; ++j) acc[j] = acc[j] + (float)code_of<BITS>(w, j) * (j < 4 ? sa : sb);
+    } else if constexpr (kDecodeF16 && BITS == 4) {
+        const uint32_t x = w.x ^ 0x88888888u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t c = (x >> (4 * j)) & 0x000F000Fu;  // codes j and j + 4
+            acc[j] = acc[j] + __builtin_fmaf(half_lo(c), sa, oa);
+            acc[j + 4] = acc[j + 4] + __builtin_fmaf(half_hi(c), sb, ob);
+        }
+    } else if constexpr (kDecodeF16 && BITS == 8) {
+        const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
+        const uint32_t c02 = x0 & 0x00FF00FFu, c13 = (x0 >> 8) & 0x00FF00FFu;
+        const uint32_t c46 = x1 & 0x00FF00FFu, c57 = (x1 >> 8) & 0x00FF00FFu;
+        acc[0] = acc[0] + __builtin_fmaf(half_lo(c02), sa, oa);
+        acc[1] = acc[1] + __builtin_fmaf(half_lo(c13), sa, oa);
+        acc[2] = acc[2] + __builtin_fmaf(half_hi(c02), sa, oa);
+        acc[3] = acc[3] + __builtin_fmaf(half_hi(c13), sa, oa);
+        acc[4] = acc[4] + __builtin_fmaf(half_lo(c46), sb, ob);
+        acc[5] = acc[5] + __builtin_fmaf(half_lo(c57), sb, ob);
+        acc[6] = acc[6] + __builtin_fmaf(half_hi(c46), sb, ob);
+        acc[7] = acc[7] + __builtin_fmaf(half_hi(c57), sb, ob);
+    } else if constexpr (BITS == 4) {
         const uint32_t x = w.x ^ 0x88888888u;
         const uint32_t lo = x & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
         const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
@@ -79,7 +122,7 @@ __device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float
         acc_byte<2>(acc[5], hi, sb, ob);
         acc_byte<3>(acc[6], lo, sb, ob);
         acc_byte<3>(acc[7], hi, sb, ob);
-    } else if constexpr (BITS == 8) {
+    } else {
         const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
         acc_byte<0>(acc[0], x0, sa, oa);
         acc_byte<1>(acc[1], x0, sa, oa);
@@ -89,9 +132,6 @@ __device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float
         acc_byte<1>(acc[5], x1, sb, ob);
         acc_byte<2>(acc[6], x1, sb, ob);
         acc_byte<3>(acc[7], x1, sb, ob);
-    } else {
-#pragma unroll
-        for (int j = 0; j < kDrVec; ++j) acc[j] = acc[j] + (float)code_of<BITS>(w, j) * (j < 4 ? sa : sb);
     }
 }
 
@@ -153,8 +193,13 @@ __device__ __forceinline__ void store4f(float* dst, int64_t i0, const float* x) 
     __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, (f32x4*)(dst + i0));
 }
 
+// The fused Adam step holds the optimizer state of its sub-tile in registers besides the
+// payload codes: capped at 5 waves per SIMD (96 VGPRs) it does not spill.
+constexpr int dr_waves_per_eu(int mode) { return mode == kDrOutAdam ? 5 : 1; }
+
 template <int BITS, int B, bool FIXED, int MODE>
-__global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
+__global__ __launch_bounds__(kDrThreads) __attribute__((amdgpu_waves_per_eu(dr_waves_per_eu(MODE))))
+void dr_kernel(DrParams p) {
     using LY = DrLayout<MODE>;
     constexpr bool SPLIT = LY::kSplit;
     constexpr int U = dr_unroll(MODE);
@@ -180,7 +225,8 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
 #pragma unroll
             for (int j = 0; j < kDrVec; ++j) acc[u][j] = 0.0f;
 
-        if (tb + TILE <= p.n) {
+        bool whole = tb + TILE <= p.n;  // false: the element-wise path below takes the tile
+        if (whole) {
             // The optimizer state is loaded first, so its latency overlaps the payloads'.
             float th[ADAM ? U : 1][kDrVec], mo[ADAM ? U : 1][kDrVec], ve[ADAM ? U : 1][kDrVec];
             if constexpr (ADAM) {
@@ -250,7 +296,19 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                     }
                     stp = am / (float)QMAX;  // 0 for an all-zero block
                 }
-                // the decoder's offset -2^(b-1)*step (exact), formed once per scale
+                // Every lane now holds one peer's step of one block (the fixed step is the
+                // same in all).  The fma forms of the decoder need |step| < 2^100 (their
+                // -2^(b-1)*step and step*2^24 must not overflow): a tile with a larger,
+                // infinite or NaN step is redone from the start by the element-wise path
+                // below, which forms q * step.
+                if constexpr (BITS != 2) {
+                    if (__builtin_amdgcn_ballot_w64(!(fabsf(stp) < 0x1p100f)) != 0) {
+                        whole = false;
+                        break;
+                    }
+                }
+                // the decoder's scale, and its offset -2^(b-1)*step (exact), once per scale
+                const float scl = (BITS != 2 && kDecodeF16) ? stp * kF16SubScale : stp;
                 const float offp = -(float)(1 << (BITS - 1)) * stp;
                 for (int q0 = 0; q0 < ng; q0 += kDrPeerBatch) {
                     if (q0 > 0) load_batch(q0);
@@ -268,11 +326,11 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                         if (q0 + b < ng) {
 #pragma unroll
                             for (int u = 0; u < U; ++u) {
-                                float sa = stp, oa = offp, sb = stp, ob = offp;
+                                float sa = scl, oa = offp, sb = scl, ob = offp;
                                 if constexpr (!FIXED) {
                                     const int a0 = src[u][0] + b * BPT * 4;
                                     sa = __builtin_bit_cast(
-                                        float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, stp)));
+                                        float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, scl)));
                                     if constexpr (BITS != 2)
                                         oa = __builtin_bit_cast(
                                             float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, offp)));
@@ -281,7 +339,7 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                                     if constexpr (TWO) {
                                         const int a1 = src[u][1] + b * BPT * 4;
                                         sb = __builtin_bit_cast(
-                                            float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, stp)));
+                                            float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, scl)));
                                         if constexpr (BITS != 2)
                                             ob = __builtin_bit_cast(
                                                 float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, offp)));
@@ -293,7 +351,9 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
                     }
                 }
             }
-            if constexpr (ADAM) {
+            if (!whole) {
+                // redone element-wise below
+            } else if constexpr (ADAM) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -315,8 +375,14 @@ __global__ __launch_bounds__(kDrThreads) void dr_kernel(DrParams p) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) store_out8<MODE>(p.out, tb + pos[u][0], tb + pos[u][1], acc[u], p.out_scale);
             }
-        } else {
-            // ragged tail: element-wise, reading only the bytes that exist
+        }
+        if (!whole) {
+            // the ragged tail, or a tile with a step of at least 2^100 or not finite:
+            // element-wise, reading only the bytes that exist, d = q * step
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < kDrVec; ++j) acc[u][j] = 0.0f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll

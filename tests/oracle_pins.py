@@ -281,6 +281,29 @@ def pin_dequant_reduce(O):
     assert np.array_equal(gotb, tb)
 
 
+def pin_dequant_huge_scales(O):
+    """Eqn. (8) at the top of the fp32 range: d = q * step stays the exact product as long
+    as it is representable (a decoder that forms it as (q + 8) * step - 8 * step
+    overflows), and a sum that leaves the range is infinite.  4-bit, blocks of 4, absmax
+    7 * 2^124 so that step = 2^124 exactly."""
+    step = 2.0 ** 124
+    am = np.array([7 * step], F32)
+    pos7 = np.array([0x77, 0x77], np.uint8)    # four codes +7
+    neg8 = np.array([0x88, 0x88], np.uint8)    # four codes -8
+    mixed = np.array([0x07, 0x8f], np.uint8)   # codes 7, 0, -1, -8
+    got = O.dequant_reduce([(pos7, am), (neg8, am)], 4, bits=4, block=4, out_scale=0.5)
+    assert np.array_equal(got, np.full(4, -step / 2, F32))          # (7 - 8) * 2^124 / 2
+    got = O.dequant_reduce([(mixed, am)], 4, bits=4, block=4, out_scale=1.0)
+    assert np.array_equal(got, np.array([7 * step, 0, -step, -8 * step], F32))
+    with np.errstate(over="ignore"):
+        got = O.dequant_reduce([(pos7, am)] * 3, 4, bits=4, block=4, out_scale=1.0)
+    assert np.all(np.isposinf(got))                                  # 21 * 2^124 > 2^128
+    # the largest block scale: 7 * fl(FLT_MAX / 7) is finite
+    fmax = np.array([np.finfo(F32).max], F32)
+    got = O.dequant_reduce([(pos7, fmax)], 4, bits=4, block=4, out_scale=1.0)
+    assert np.all(np.isfinite(got)) and np.all(got == F32(7) * (fmax[0] / F32(7)))
+
+
 # -- P-11: all-zero blocks ---------------------------------------------------------------------
 
 def pin_zero_blocks(O):
@@ -780,5 +803,5 @@ ALL_PINS = [
     pin_i8_error_accounting, pin_i8_equals_float_when_exact, pin_reset, pin_i8_compressor_vs_torch,
     pin_sa_worked, pin_sa_brute_force, pin_sa_dense_equivalent, pin_sa_transmits_topk,
     pin_adam_worked, pin_adam_closed_form, pin_adam_limits, pin_cq_scalar_twin, pin_dr_scalar_twin,
-    pin_dra_worked, pin_tiny_scales, pin_topk_tiny_scales,
+    pin_dra_worked, pin_tiny_scales, pin_topk_tiny_scales, pin_dequant_huge_scales,
 ]

@@ -206,6 +206,12 @@ def _recip_zero_subnormal(step):
     return np.where(step >= np.finfo(step.dtype).tiny, inv, step.dtype.type(0)).astype(step.dtype)
 
 
+def _dequant_offset_form(q, step_per_elem):
+    # q * step formed as (q + 8) * step - 8 * step, each product rounded
+    ft = step_per_elem.dtype.type
+    return (q + 8).astype(step_per_elem.dtype) * step_per_elem - ft(8) * step_per_elem
+
+
 MUTATIONS = {
     "error_update drops beta*e": ("error_update", _drop_beta_term),
     "error_update swaps beta and 1-beta": ("error_update", _swap_weights),
@@ -236,6 +242,7 @@ MUTATIONS = {
     "bf16 weight copy truncated": ("dequant_reduce_adam", _dra_copy_truncated),
     "tiny block keeps an infinite reciprocal": ("finite_reciprocal", _recip_keeps_overflow),
     "reciprocal zeroed for every subnormal step": ("finite_reciprocal", _recip_zero_subnormal),
+    "decompressor as a biased product minus its offset": ("dequantize", _dequant_offset_form),
 }
 
 
