@@ -167,7 +167,9 @@ typedef struct {
  *   out[i] = acc * out_scale                      (out_scale = 1/N for the average)
  * with step_p = absmax_p[block of i] / qmax (0 for an all-zero block), or 1/s in
  * fixed-scale mode.  The accumulator lives in registers; bf16 output rounds to
- * nearest even.
+ * nearest even.  Every product and sum is the IEEE fp32 result for any absmax value,
+ * up to FLT_MAX and including inf and NaN (a tile whose step is 2^100 or more, or not
+ * finite, takes a slower element-wise path).
  *   peers      host array of npeers payloads, 1 <= npeers <= LOCO_MAX_PEERS
  *   n          elements of the partition (>= 0; 0 is a no-op)
  *   bits       2, 4 or 8;  block  64, 128, 256 or 512 (ignored when fixed_scale > 0)
