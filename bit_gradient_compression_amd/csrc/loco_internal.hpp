@@ -204,7 +204,7 @@ inline hipError_t compute_units(int& cus) {
 // ---- sparse aggregation ------------------------------------------------------------
 
 #ifndef LOCO_SA_WG_PER_CU_F32
-#define LOCO_SA_WG_PER_CU_F32 3
+#define LOCO_SA_WG_PER_CU_F32 0
 #endif
 #ifndef LOCO_SA_WG_PER_CU_BF16
 #define LOCO_SA_WG_PER_CU_BF16 8
@@ -223,7 +223,12 @@ constexpr int kSaThreadsBf16 = LOCO_SA_THREADS_BF16;  // threads per chunk, bf16
 constexpr int kSaPeerBatch = 8;  // peers whose first slot is loaded together
 // Workgroups per compute unit of the persistent grid, per output type: each workgroup
 // takes every gridDim.x-th chunk and loads the next chunk's payload while it processes
-// the current one (0: one workgroup per chunk, no prefetch).
+// the current one (0: the general kernel, one workgroup per chunk, after a pre-read).
+// Measured on 8 peers of 2^28 in chunks of 4096 (back to back / cache-flushed, ms): fp32
+// out 0.195 / 0.193 with the general kernel and one pre-read, against 0.203 / 0.213 with
+// 3 persistent workgroups per compute unit and 0.178 / 0.240 for the general kernel
+// without the pre-read; bf16 out 0.116 / 0.127 with 8 persistent workgroups, against
+// 0.127 / 0.130 with the general kernel and a pre-read.
 constexpr int kSaWgPerCuF32 = LOCO_SA_WG_PER_CU_F32;
 constexpr int kSaWgPerCuBf16 = LOCO_SA_WG_PER_CU_BF16;
 #ifndef LOCO_SA_PASS_BYTES_F32
@@ -241,6 +246,19 @@ constexpr int kSaWgPerCuBf16 = LOCO_SA_WG_PER_CU_BF16;
 // in one pass, 0.154 in two.
 constexpr long long kSaPassBytesF32 = LOCO_SA_PASS_BYTES_F32;
 constexpr long long kSaPassBytesBf16 = LOCO_SA_PASS_BYTES_BF16;
+// The general kernel (one workgroup per chunk): payload bytes per launch, each launch
+// preceded by a pre-read of its chunks' payloads into the caches (0: one launch, no
+// pre-read).  fp32 out, 8 peers of 2^28 (99 MB of payloads), back to back / flushed, ms:
+// one pre-read of all of it 0.195 / 0.193; launches of <= 64 MB 0.197 / 0.200, <= 32 MB
+// 0.201 / 0.207.
+#ifndef LOCO_SA_PREREAD_BYTES_F32
+#define LOCO_SA_PREREAD_BYTES_F32 (128LL << 20)
+#endif
+#ifndef LOCO_SA_PREREAD_BYTES_BF16
+#define LOCO_SA_PREREAD_BYTES_BF16 0
+#endif
+constexpr long long kSaPrereadBytesF32 = LOCO_SA_PREREAD_BYTES_F32;
+constexpr long long kSaPrereadBytesBf16 = LOCO_SA_PREREAD_BYTES_BF16;
 
 struct SaPeerDev {
     const uint16_t* idx;

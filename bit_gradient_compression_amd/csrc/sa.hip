@@ -16,11 +16,13 @@
 // barrier between them, so every element adds its contributions in peer order.  Within
 // one peer the slots name distinct elements, so their read-add-writes never collide.  The
 // dense chunk is then written once, each thread storing whole runs of up to 8 outputs.
-// Two kernels: a streaming one (k <= NT, at most kSaPeerBatch peers: the usual case), a
-// persistent grid of a few workgroups per compute unit that loads each chunk's payload
-// while it processes the previous chunk, and first reads the payloads of many chunks in a
-// read-only pass so that its output writes meet no DRAM reads; and a general one, one
-// workgroup per chunk.
+// Two kernels: a streaming one (k <= NT, at most kSaPeerBatch peers), a persistent grid
+// of a few workgroups per compute unit that loads each chunk's payload while it processes
+// the previous chunk, and first reads the payloads of many chunks in a read-only pass so
+// that its output writes meet no DRAM reads (taken for bf16 output); and a general one,
+// one workgroup per chunk, preceded by a pre-read kernel over the payloads of the chunks
+// it covers, for the same reason (taken for fp32 output, and whenever the streaming one
+// does not apply).
 
 #include "loco_device.hpp"
 #include "loco_internal.hpp"
@@ -232,6 +234,34 @@ __device__ __forceinline__ void read_pass_range(const void* base, int64_t lo, in
 // s_waitcnt vmcnt(0), the other counters left as they are (expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmcnt0 = 0x0f70;
 
+// The whole 16-byte vectors of bytes [lo, hi) of one payload array of `total` bytes,
+// read into the caches by the threads of the grid (thread `first` of `stride`).
+__device__ __forceinline__ void read_range_grid(const void* base, int64_t lo, int64_t hi, int64_t total,
+                                                int64_t first, int64_t stride, uint32_t lds) {
+    const int64_t v1 = min((hi + 15) / 16, total / 16);
+    const u32x4* v = (const u32x4*)base;
+    for (int64_t i = lo / 16 + first; i < v1; i += stride) read_to_lds16(v + i, lds);
+}
+
+// Pre-read for the general kernel: reads every peer's payload of chunks [c0, c1) into the
+// caches, so that the aggregation launched next on the stream finds it there and its
+// output writes meet no DRAM reads.
+template <int NT>
+__global__ __launch_bounds__(NT) void sa_preread_kernel(SaParams p, int64_t c0, int64_t c1) {
+    __shared__ __attribute__((aligned(16))) uint32_t land[64 * 4];  // one wave's 16-byte loads
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)land;
+    const int64_t kb = 2 * (int64_t)p.k, cb = p.cbytes;
+    const int64_t first = (int64_t)blockIdx.x * NT + threadIdx.x, stride = (int64_t)gridDim.x * NT;
+    for (int q = 0; q < p.npeers; ++q) {
+        const SaPeerDev pe = p.peer[q];
+        read_range_grid(pe.idx, c0 * kb, c1 * kb, p.nchunks * kb, first, stride, lds);
+        read_range_grid(pe.codes, c0 * cb, c1 * cb, p.nchunks * cb, first, stride, lds);
+        read_range_grid(pe.absmax, c0 * 4, c1 * 4, p.nchunks * 4, first, stride, lds);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+}
+constexpr int kSaPrereadThreads = 256;
+
 // General kernel: one workgroup per chunk of [c0, c1), any k and number of peers.
 template <int C, int BITS, bool OBF, int NT>
 __global__ __launch_bounds__(NT) void sa_kernel(SaParams p, int64_t c0, int64_t c1) {
@@ -318,12 +348,14 @@ __global__ __launch_bounds__(NT) void sa_stream_kernel(SaParams p) {
     }
 }
 
-// Launch shape per output type, measured on MI355X for 8 peers of 2^28 in chunks of 4096,
-// with the read passes (cache-cold / back to back): 128 threads per chunk; fp32 out with
-// 3 workgroups per compute unit 0.211 / 0.206 ms, against 0.331 / 0.330 with 1, 0.258 /
-// 0.245 with 2, 0.241 / 0.229 with 4 and 0.241 / 0.221 with 6; bf16 out with 8, 0.130 /
-// 0.117 ms.  The output is ~92% of the bytes, and dense writes run best with few waves in
-// flight, but fewer than 3 workgroups leave the payload loads' latency exposed.
+// Launch shape per output type, measured on MI355X for 8 peers of 2^28 in chunks of 4096
+// (cache-cold / back to back): 128 threads per chunk.  The streaming kernel with its read
+// passes, fp32 out: 3 workgroups per compute unit 0.211 / 0.206 ms, against 0.331 / 0.330
+// with 1, 0.258 / 0.245 with 2, 0.241 / 0.229 with 4 and 0.241 / 0.221 with 6; the
+// general kernel after one pre-read beats it (0.193 / 0.195), and is what fp32 output
+// takes.  bf16 out: the streaming kernel with 8, 0.127 / 0.116 ms.  The output is ~92% of
+// the bytes; a persistent grid with few waves in flight leaves the payload loads' latency
+// exposed, one workgroup per chunk hides it once the payloads are in the caches.
 template <int C, int BITS>
 void pick_out(bool out_bf16, bool stream, const void*& k) {
     if (stream)
@@ -376,12 +408,30 @@ hipError_t launch_sa(const SaParams& p, int chunk, int bits, bool out_bf16, hipS
         void* args[] = {(void*)&q};
         return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
     }
-    // one workgroup per chunk, chunks [c0, c1) per launch
-    for (int64_t c0 = 0; c0 < p.nchunks; c0 += kMaxGrid) {
-        int64_t c1 = p.nchunks - c0 < kMaxGrid ? p.nchunks : c0 + kMaxGrid;
-        const int64_t blocks = c1 - c0;
+    // one workgroup per chunk, chunks [c0, c1) per launch; with a pre-read budget, each
+    // launch covers chunks whose payloads fit it and is preceded by their pre-read
+    const long long pre = out_bf16 ? kSaPrereadBytesBf16 : kSaPrereadBytesF32;
+    const int64_t per_chunk = (int64_t)p.npeers * (2 * (int64_t)p.k + p.cbytes + 4);
+    int64_t span = pre > 0 ? (int64_t)(pre / per_chunk) : kMaxGrid;
+    span = span < 1 ? 1 : (span > kMaxGrid ? kMaxGrid : span);
+    int cus = 0;
+    if (pre > 0) {
+        const hipError_t err = compute_units(cus);
+        if (err != hipSuccess) return err;
+    }
+    for (int64_t c0 = 0; c0 < p.nchunks; c0 += span) {
+        int64_t c1 = p.nchunks - c0 < span ? p.nchunks : c0 + span;
         void* args[] = {(void*)&p, (void*)&c0, (void*)&c1};
-        const hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
+        if (pre > 0) {
+            const int64_t vecs = (c1 - c0) * per_chunk / 16 + 3 * (int64_t)p.npeers;
+            int64_t pb = (vecs + kSaPrereadThreads - 1) / kSaPrereadThreads;
+            if (pb > (int64_t)cus * 8) pb = (int64_t)cus * 8;
+            if (pb < 1) pb = 1;
+            const hipError_t err = hipLaunchKernel((const void*)&sa_preread_kernel<kSaPrereadThreads>,
+                                                   dim3((unsigned)pb), dim3(kSaPrereadThreads), args, 0, stream);
+            if (err != hipSuccess) return err;
+        }
+        const hipError_t err = hipLaunchKernel(k, dim3((unsigned)(c1 - c0)), dim3(threads), args, 0, stream);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;
