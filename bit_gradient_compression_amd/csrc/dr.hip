@@ -194,7 +194,7 @@ __device__ __forceinline__ void store4f(float* dst, int64_t i0, const float* x) 
 }
 
 // The fused Adam step holds the optimizer state of its sub-tile in registers besides the
-// payload codes: capped at 5 waves per SIMD (96 VGPRs) it does not spill.
+// payload codes: it needs 94 VGPRs, 5 waves per SIMD (the cap keeps it from spilling).
 constexpr int dr_waves_per_eu(int mode) { return mode == kDrOutAdam ? 5 : 1; }
 
 template <int BITS, int B, bool FIXED, int MODE>
@@ -378,7 +378,12 @@ void dr_kernel(DrParams p) {
         }
         if (!whole) {
             // the ragged tail, or a tile with a step of at least 2^100 or not finite:
-            // element-wise, reading only the bytes that exist, d = q * step
+            // element-wise, reading only the bytes that exist, d = q * step.  Its element
+            // offsets derive from a lane index the compiler cannot see through, so they are
+            // formed here rather than hoisted out of the tile loop (where they would stay
+            // live, or be spilled, on every tile).
+            int lane_e = lane;
+            asm volatile("" : "+v"(lane_e));
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -387,7 +392,7 @@ void dr_kernel(DrParams p) {
             for (int u = 0; u < U; ++u) {
 #pragma unroll
                 for (int pc = 0; pc < 2; ++pc) {
-                    const int64_t i0 = tb + pos[u][pc];
+                    const int64_t i0 = tb + (u * SUB + LY::piece(lane_e, pc));
                     const int64_t left = p.n - i0;
                     const int nvalid = left <= 0 ? 0 : (left >= 4 ? 4 : (int)left);
                     if (nvalid == 0) continue;

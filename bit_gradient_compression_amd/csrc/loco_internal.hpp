@@ -43,10 +43,8 @@ namespace loco {
 #ifndef LOCO_DR_THREADS
 #define LOCO_DR_THREADS 256
 #endif
-// Top-k: 6 waves per SIMD caps the kernel at 80 VGPRs (two values of the chunk's
-// prologue are spilled and reloaded once at its end).  Measured on 2^28 fp32, chunk
-// 4096, k 82, 2-bit, back to back / flushed: 0.530 / 0.520 ms, against 0.561 / 0.558
-// at 5 waves (96 VGPRs) and 0.559 / 0.547 at 4.
+// Top-k: at least 6 waves per SIMD.  Since each workgroup takes one chunk and nothing is
+// carried from chunk to chunk, the kernel needs 60 VGPRs and spills nothing.
 #ifndef LOCO_TK_WAVES_PER_EU
 #define LOCO_TK_WAVES_PER_EU 6
 #endif
@@ -162,7 +160,7 @@ hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, int mod
 // Candidate list capacity of the fast selection path.
 constexpr int kTkCap = 512;
 
-// Workgroups of one Top-k launch (one 256-thread workgroup per chunk at a time).
+// Workgroups of one Top-k launch (one 256-thread workgroup per chunk).
 constexpr int64_t kTkMaxGrid = 1 << 20;
 
 struct TkParams {

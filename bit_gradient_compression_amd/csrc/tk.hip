@@ -489,26 +489,21 @@ __device__ __forceinline__ void tk_chunk(const TkParams& p, int64_t chunk, TkSha
     if (tid == 0) p.absmax[chunk] = absmax;
 }
 
-// Grid-strides over chunks [c0, c1); the barrier at the end of each chunk lets the next
-// one reuse the LDS staging.  Full chunks and the short last chunk are separate kernels,
-// so the full-chunk code carries no bounds masks (registers are allocated per kernel).
-// (Measured on MI355X: one workgroup per chunk beats a persistent grid that loads the
-// next chunk while processing the current one, 0.61 against 0.66-0.68 ms on 2^28.)
+// Workgroup b takes chunk c0 + b of [c0, c1).  One chunk per workgroup and no loop, so no
+// lane address is kept live (or spilled) across chunks.  Full chunks and the short last
+// chunk are separate kernels, so the full-chunk code carries no bounds masks (registers
+// are allocated per kernel).  (Measured on MI355X: one workgroup per chunk beats a
+// persistent grid that loads the next chunk while processing the current one, 0.61
+// against 0.66-0.68 ms on 2^28.)
 template <int VPT, int BITS, bool FULL>
 __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(LOCO_TK_WAVES_PER_EU)))
 void tk_kernel(TkParams p, int64_t c0, int64_t c1) {
     __shared__ TkShared<kTkThreads * VPT> sh;
-    int64_t c = c0 + blockIdx.x;
+    const int64_t c = c0 + blockIdx.x;
     if (c >= c1) return;
     float gv[TkShape<VPT>::Q][TkShape<VPT>::R], ev[TkShape<VPT>::Q][TkShape<VPT>::R];
     tk_load<VPT, FULL>(p, c, gv, ev);
-    for (;;) {
-        tk_chunk<VPT, BITS, FULL>(p, c, sh, gv, ev);
-        c += gridDim.x;
-        if (c >= c1) break;
-        __syncthreads();
-        tk_load<VPT, FULL>(p, c, gv, ev);
-    }
+    tk_chunk<VPT, BITS, FULL>(p, c, sh, gv, ev);
 }
 
 template <int BITS, bool FULL>
@@ -541,11 +536,11 @@ hipError_t launch_tk(const TkParams& p, int chunk, int bits, hipStream_t stream)
     if (!kfull || !ktail) return hipErrorInvalidValue;
     int64_t nfull = p.n / chunk;
     int64_t nall = (p.n + chunk - 1) / chunk;
-    if (nfull > 0) {
-        int64_t c0 = 0;
-        const int64_t grid = nfull < kTkMaxGrid ? nfull : kTkMaxGrid;
-        void* args[] = {(void*)&p, (void*)&c0, (void*)&nfull};
-        const hipError_t st = hipLaunchKernel(kfull, dim3((unsigned)grid), dim3(kTkThreads), args, 0, stream);
+    // whole chunks, at most kTkMaxGrid per launch
+    for (int64_t c0 = 0; c0 < nfull; c0 += kTkMaxGrid) {
+        int64_t c1 = nfull - c0 < kTkMaxGrid ? nfull : c0 + kTkMaxGrid;
+        void* args[] = {(void*)&p, (void*)&c0, (void*)&c1};
+        const hipError_t st = hipLaunchKernel(kfull, dim3((unsigned)(c1 - c0)), dim3(kTkThreads), args, 0, stream);
         if (st != hipSuccess) return st;
     }
     if (nall > nfull) {
