@@ -7,7 +7,9 @@ kept, and no packed-fp32 instructions.
 
 from __future__ import annotations
 
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -50,6 +52,27 @@ def _run(cmd):
     return r
 
 
+# The compiler's per-kernel resource remarks (-Rpass-analysis=kernel-resource-usage), kept
+# as one JSON file per build: VGPRs, scratch bytes per lane, occupancy and LDS per kernel.
+RESOURCE_FLAG = "-Rpass-analysis=kernel-resource-usage"
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                     r"LDS Size \[bytes/block\]|VGPRs Spill):\s+(\S+)")
+_KEYS = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch_bytes_per_lane",
+         "Occupancy [waves/SIMD]": "waves_per_simd", "LDS Size [bytes/block]": "lds_bytes", "VGPRs Spill": "vgpr_spill"}
+
+
+def parse_resources(text: str) -> dict:
+    """Kernel name -> its resource figures, from the compiler's remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(text):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[_KEYS[key]] = int(val)
+    return out
+
+
 def build(out_path: str = LIB_PATH, extra_flags=(), jobs: int | None = None, verbose=False,
           build_dir: str = BUILD_DIR, twins_path: str | None = TWINS_PATH) -> str:
     """Compile and link the library (and, unless twins_path is None, the benchmark's
@@ -62,12 +85,16 @@ def build(out_path: str = LIB_PATH, extra_flags=(), jobs: int | None = None, ver
     for src in SOURCES + (TWINS_SOURCES if twins_path else []):
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *flags, RESOURCE_FLAG, "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))
+    resources = {}
     with ThreadPoolExecutor(jobs) as ex:
-        for r in ex.map(_run, cmds):
+        for src, r in zip(SOURCES + (TWINS_SOURCES if twins_path else []), ex.map(_run, cmds)):
+            resources.update({k: {**v, "source": src} for k, v in parse_resources(r.stderr).items()})
             if verbose and r.stderr:
                 print(r.stderr, file=sys.stderr)
+    with open(os.path.join(build_dir, "resources.json"), "w") as f:
+        json.dump(resources, f, indent=0, sort_keys=True)
     links = [(out_path, objs[:len(SOURCES)])]
     if twins_path:
         links.append((twins_path, objs[len(SOURCES):]))
