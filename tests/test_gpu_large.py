@@ -120,9 +120,42 @@ def test_topk_past_2p31(gpu_lib):
     say(f"  {len(ranges)} chunks checked over 2 steps")
 
 
+def test_topk_more_chunks_than_one_launch(gpu_lib):
+    """2^20 + 3 whole chunks of 256 and a short one (n = 2^28 + 818): the whole chunks take
+    two launches of at most 2^20 workgroups; the chunks on both sides of the launch
+    boundary, the first and the short last one are checked, over 2 steps."""
+    C, k, bits = 256, 5, 2
+    n = (1 << 20) * C + 3 * C + 50
+    chunks = -(-n // C)
+    nb = gpu_lib.code_bytes(k, bits)
+    e = torch.zeros(n, device="cuda")
+    idx = torch.empty(chunks * k, dtype=torch.int16, device="cuda")
+    codes = torch.empty(chunks * nb, dtype=torch.uint8, device="cuda")
+    am = torch.empty(chunks, device="cuda")
+    check = [0, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, chunks - 2, chunks - 1]
+    ora_e = {c: np.zeros(min((c + 1) * C, n) - c * C, np.float32) for c in check}
+    for step in range(2):
+        say(f"top-k over two launches: step {step}, n={n:,}, {chunks:,} chunks of {C}")
+        g = W.sparseloco_grad(step, n=n, device="cuda")
+        gpu_lib.loco_topk_quantize(g, e, chunk=C, k=k, idx=idx, codes=codes, absmax=am, bits=bits, ef_decay=1.0)
+        torch.cuda.synchronize()
+        for c in check:
+            lo, hi = c * C, min((c + 1) * C, n)
+            ref = oracle.topk_quantize(host(g[lo:hi]), ora_e[c], chunk=C, k=k, bits=bits, decay=1.0)
+            t = f"step {step} chunk {c} (elements {lo:,}..{hi:,})"
+            assert_bytes_equal(host(idx[c * k:(c + 1) * k]).view(np.uint16), ref["idx"], f"{t} idx")
+            assert_bytes_equal(host(codes[c * nb:(c + 1) * nb]), ref["codes"], f"{t} codes")
+            assert_bytes_equal(host(am[c:c + 1]).view(np.uint32), ref["absmax"].view(np.uint32), f"{t} absmax")
+            assert_f32_close(host(e[lo:hi]), ref["e_new"], np.full(hi - lo, float(ref["absmax"][0])), f"{t} error")
+            ora_e[c] = ref["e_new"]
+        del g
+    say(f"  {len(check)} chunks checked over 2 steps")
+
+
 def test_sparse_aggregate_past_2p31(gpu_lib):
     """2 peers' Top-k payloads of 2^31 + 4096 + 33 elements (chunk 4096, k = 82, 2-bit) into
-    fp32 x 1/2: the streaming kernel's chunks past 2^31 and its short last chunk."""
+    fp32 x 1/2: chunks past 2^31, the short last chunk, and (fp32 output) launches of at
+    most 128 MB of payload, each after its pre-read (two here)."""
     n, C, k, bits, P = BIG + 4096 + 33, 4096, 82, 2, 2
     cb = gpu_lib.code_bytes(k, bits)
     say(f"sparse aggregate past 2^31: n={n:,}, generating {P} payloads")
