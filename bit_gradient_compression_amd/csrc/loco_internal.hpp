@@ -11,8 +11,8 @@ namespace loco {
 // ---- compensate-quantize -----------------------------------------------------------
 
 // Launch shape of the streaming kernels.  The grid is not persistent: each wave takes one
-// tile and exits, so the waves in flight sweep memory in address order; the grid-stride
-// loop only matters past kMaxGrid workgroups.
+// tile and exits, so the waves in flight sweep memory in address order.  Past kMaxGrid
+// workgroups, compensate-quantize launches again; dequant-reduce grid-strides.
 #ifndef LOCO_CQ_UNROLL
 #define LOCO_CQ_UNROLL 1
 #endif
