@@ -194,12 +194,15 @@ __device__ __forceinline__ void store4f(float* dst, int64_t i0, const float* x) 
 }
 
 // The fused Adam step holds the optimizer state of its sub-tile in registers besides the
-// payload codes: it needs 94 VGPRs, 5 waves per SIMD (the cap keeps it from spilling).
-constexpr int dr_waves_per_eu(int mode) { return mode == kDrOutAdam ? 5 : 1; }
+// payload codes: 84 VGPRs, 5 waves per SIMD (capped at 6 it spills).
+#ifndef LOCO_DRA_WAVES_PER_EU
+#define LOCO_DRA_WAVES_PER_EU 5
+#endif
+constexpr int dr_waves_per_eu(int mode) { return mode == kDrOutAdam ? LOCO_DRA_WAVES_PER_EU : 1; }
 
 template <int BITS, int B, bool FIXED, int MODE>
 __global__ __launch_bounds__(kDrThreads) __attribute__((amdgpu_waves_per_eu(dr_waves_per_eu(MODE))))
-void dr_kernel(DrParams p) {
+void dr_kernel(DrParams p, int64_t tbase) {
     using LY = DrLayout<MODE>;
     constexpr bool SPLIT = LY::kSplit;
     constexpr int U = dr_unroll(MODE);
@@ -208,7 +211,6 @@ void dr_kernel(DrParams p) {
     static_assert(TILE % B == 0, "a wave tile spans whole scale blocks");
     constexpr int SUB = 64 * kDrVec;
     const int lane = lane_id();
-    const int64_t nwaves = (int64_t)gridDim.x * (kDrThreads / kWave);
     const int64_t wg = xcd_remap<kXcds, kDrXcdRun>(blockIdx.x, gridDim.x);
     // element offsets, within the tile, of the lane's pieces in each sub-tile
     int pos[U][2];
@@ -216,8 +218,9 @@ void dr_kernel(DrParams p) {
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int pc = 0; pc < 2; ++pc) pos[u][pc] = u * SUB + LY::piece(lane, pc);
-    for (int64_t t = wg * (kDrThreads / kWave) + uniform(threadIdx.x / kWave); t < p.ntiles;
-         t += nwaves) {
+    const int64_t t = tbase + wg * (kDrThreads / kWave) + uniform(threadIdx.x / kWave);
+    if (t >= p.ntiles) return;
+    {
         const int64_t tb = t * TILE;  // the tile's first element
         float acc[U][kDrVec];
 #pragma unroll
@@ -475,12 +478,17 @@ hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, int mod
         case kDrOutAdam: k = pick_fixed<kDrOutAdam>(fixed, bits, block); break;
     }
     if (!k) return hipErrorInvalidValue;
+    // one wave per tile; launches of at most kMaxGrid workgroups
     const int64_t waves_per_block = kDrThreads / kWave;
-    int64_t blocks = (p.ntiles + waves_per_block - 1) / waves_per_block;
-    if (blocks > kMaxGrid) blocks = kMaxGrid;
-    if (blocks < 1) blocks = 1;
-    void* args[] = {(void*)&p};
-    return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(kDrThreads), args, 0, stream);
+    const int64_t per_launch = kMaxGrid * waves_per_block;
+    for (int64_t tbase = 0; tbase < p.ntiles; tbase += per_launch) {
+        const int64_t tiles = p.ntiles - tbase < per_launch ? p.ntiles - tbase : per_launch;
+        const int64_t blocks = (tiles + waves_per_block - 1) / waves_per_block;
+        void* args[] = {(void*)&p, (void*)&tbase};
+        const hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(kDrThreads), args, 0, stream);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace loco
