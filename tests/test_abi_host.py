@@ -367,3 +367,17 @@ def test_header_compiles_and_links_from_c(lib, tmp_path, lang):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and "bad=0" in r.stdout, r.stdout + r.stderr
+
+
+def test_twins_library_is_separate_and_loads():
+    """The benchmark's traffic twins live in their own library: it loads, exports its five
+    entry points, and refuses a shape it has no twin for before any launch."""
+    from bit_gradient_compression_amd import twins
+    if not os.path.exists(B.TWINS_PATH):
+        pytest.fail("libloco_twins.so is not built (run __graft_entry__.build())")
+    tl = twins.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", B.TWINS_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(loco_\w+)$", out, flags=re.M))
+    assert exported == {"loco_twin_copy", "loco_twin_cq", "loco_twin_dr", "loco_twin_tk", "loco_twin_sa"}
+    assert tl.loco_twin_copy(None, None, 0, None) == -1
+    assert tl.loco_twin_cq(None, None, None, None, 0, 2, 0, 4, 256, None) == -1
