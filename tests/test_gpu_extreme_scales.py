@@ -1,5 +1,5 @@
-"""GPU parity of dequant-reduce and the fused Adam step at extreme block scales
-(LoCo Sec. 3.3, Eqn. (8); Sec. 4, Eqn. (9)).
+"""GPU parity of dequant-reduce, the fused Adam step and the sparse aggregation at extreme
+block scales (LoCo Sec. 3.3, Eqn. (8); Sec. 4, Eqn. (9); SparseLoCo's aggregation).
 
 The kernels' fast decoder forms fl(q * step) as one fma against the offset
 -2^(b-1) * step (and, at 4 and 8 bits, a step scaled by 2^24), which would overflow for a
@@ -163,3 +163,31 @@ def test_dra_extreme_scales(gpu_lib, bits, block):
         for b, nm in ((th, "theta"), (m, "m"), (v, "v"), (tb, "theta bf16")):
             b.check(f"{tag} {nm}")
         o_th, o_m, o_v = ref["theta"], ref["m"], ref["v"]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("od", ["f32", "bf16"])
+def test_sa_extreme_scales(gpu_lib, bits, od):
+    """Sparse aggregation (SparseLoCo) of 8 peers whose chunk scales mix ordinary and extreme
+    values (the same mix as above, per chunk): fp32 output through the pre-read and the
+    general kernel, bf16 output through the streaming kernel; bitwise, NaN-aware."""
+    n, chunk, k, npeers = 300 * 1024 + 77, 1024, 41, 8
+    nch = -(-n // chunk)
+    say(f"sparse aggregation extreme scales bits={bits} out={od}")
+    pays = []
+    for p in range(npeers):
+        ix, c, _ = W.random_sparse_payload(n, chunk, k, bits, key=("extreme-sa", bits, od, p))
+        a = extreme_absmax(nch, bits, W.seed_of("extreme-sa-absmax", bits, od, p) % 2 ** 32, region=8)
+        pays.append((ix, c, torch.from_numpy(a)))
+    out = Guarded(n, torch.float32 if od == "f32" else torch.bfloat16)
+    gpu_lib.loco_sparse_aggregate([(ix.cuda(), c.cuda(), a.cuda()) for ix, c, a in pays], n, chunk=chunk, k=k,
+                                  bits=bits, out=out.t, out_scale=1.0 / npeers)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = oracle.sparse_aggregate([(ix.numpy().view(np.uint16), c.numpy(), a.numpy()) for ix, c, a in pays], n,
+                                       chunk=chunk, k=k, bits=bits, out_scale=1.0 / npeers, out_dtype=od)
+    out.check("out")
+    if od == "f32":
+        assert_f32_nan_aware(host(out.t), want, f"bits={bits}")
+    else:
+        assert_bf16_nan_aware(bf16_bits(out.t), want, f"bits={bits}")
