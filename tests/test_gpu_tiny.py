@@ -1,4 +1,5 @@
-"""GPU parity on blocks too small for a finite reciprocal (LoCo Sec. 3.1, Eqn. (1)).
+"""GPU parity on blocks too small for a finite reciprocal (LoCo Sec. 3.1, Eqn. (1)), and
+on blocks near the top of the fp32 range.
 
 A block whose absmax is below about qmax * 2^-128 has a step whose reciprocal overflows
 fp32; both sides then take inv = 0, send zero codes and keep the block's values in the
@@ -59,3 +60,38 @@ def test_tk_tiny_chunks(gpu_lib, bits):
     say(f"tk tiny chunks bits={bits}")
     run_tk_chain(gpu_lib, 20 * 1024 + 300, 1024, 41, bits, 1.0, 3,
                  lambda step, n: tiny_values(step, n, 1024, seed=77 + bits), f"tiny b{bits}")
+
+
+def huge_values(step, n, block, seed):
+    """Per block of `block` elements: 60% of magnitude log-uniform in [1e30, 3e38] (values
+    uniform in +-that, below FLT_MAX / 1.2 so that h = g + e stays finite), 10% all zero,
+    30% N(0, 1e-3)."""
+    rng = np.random.default_rng([seed, step])
+    nb = -(-n // block)
+    kind = rng.random(nb)
+    amp = np.exp(rng.uniform(np.log(1e30), np.log(2.8e38), nb))
+    x = np.empty(nb * block, np.float64)
+    for b in range(nb):
+        sl = slice(b * block, (b + 1) * block)
+        if kind[b] < 0.6:
+            x[sl] = rng.uniform(-1, 1, block) * amp[b]
+        elif kind[b] < 0.7:
+            x[sl] = 0.0
+        else:
+            x[sl] = rng.standard_normal(block) * 1e-3
+    return torch.from_numpy(x[:n].astype(np.float32))
+
+
+@pytest.mark.filterwarnings("ignore:overflow encountered in multiply:RuntimeWarning")
+@pytest.mark.parametrize("gd", ["f32", "bf16"])
+@pytest.mark.parametrize("ed", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_cq_huge_blocks(gpu_lib, gd, ed, bits):
+    """Block scales up to ~2.8e38: steps, (subnormal) reciprocals, codes and the error update
+    stay the oracle's.  The 8-bit error's e * s_e overflows to inf there and clamps to 127
+    on both sides (the oracle's overflow warning is expected)."""
+    block = 128
+    sizes = [block * 37 + 5, 3 * 512 + 64]
+    say(f"cq huge blocks {gd}/{ed} bits={bits}")
+    gen = lambda step, n: huge_values(step, n, block, seed=bits * 100 + 7).to(TD[gd])  # noqa: E731
+    run_chain(gpu_lib, sizes, gd, ed, bits, block, 0.9, 3, gen=gen, err_scale=2.0 ** 17 if ed == "i8" else 0.0)
