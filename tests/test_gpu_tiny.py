@@ -95,3 +95,12 @@ def test_cq_huge_blocks(gpu_lib, gd, ed, bits):
     say(f"cq huge blocks {gd}/{ed} bits={bits}")
     gen = lambda step, n: huge_values(step, n, block, seed=bits * 100 + 7).to(TD[gd])  # noqa: E731
     run_chain(gpu_lib, sizes, gd, ed, bits, block, 0.9, 3, gen=gen, err_scale=2.0 ** 17 if ed == "i8" else 0.0)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_tk_huge_chunks(gpu_lib, bits):
+    """Top-k chunks whose selected values reach ~2.8e38: the chunk step, its (subnormal)
+    reciprocal, the codes and the error feedback stay the oracle's."""
+    say(f"tk huge chunks bits={bits}")
+    run_tk_chain(gpu_lib, 20 * 1024 + 300, 1024, 41, bits, 1.0, 3,
+                 lambda step, n: huge_values(step, n, 1024, seed=91 + bits), f"huge b{bits}")
