@@ -16,16 +16,17 @@ namespace loco {
 #ifndef LOCO_CQ_UNROLL
 #define LOCO_CQ_UNROLL 1
 #endif
-// An 8-bit error moves 4.5 bytes per element and spends ~22 VALU instructions on it, so
-// its waves take 2 sub-tiles (57 VGPRs, 8 waves per SIMD) and XCD runs of 64: 0.674 ms on
-// the 7B shard, against 0.70 with 4 sub-tiles (5 waves) and 0.78 with 1.
+// An 8-bit error moves 4.5 bytes per element and spends ~25 VALU instructions on it, so
+// its waves take 2 sub-tiles (50 VGPRs, 8 waves per SIMD) and XCD runs of 64: measured
+// when chosen, 0.674 ms on the 7B shard against 0.70 with 4 sub-tiles (5 waves) and 0.78
+// with 1.
 #ifndef LOCO_CQ_UNROLL_I8
 #define LOCO_CQ_UNROLL_I8 2
 #endif
 #ifndef LOCO_CQ_XCD_RUN_I8
 #define LOCO_CQ_XCD_RUN_I8 64
 #endif
-// A bf16 error (6.5 B per element) keeps 1 sub-tile per wave (40 VGPRs) and XCD runs of
+// A bf16 error (6.5 B per element) keeps 1 sub-tile per wave (32 VGPRs) and XCD runs of
 // 32: the MoE experts' 1,409,286,144 elements take 1.46-1.47 ms, against 1.48-1.53 with 2
 // or 4 sub-tiles (runs of 32 or 64) and 1.50-1.52 with runs of 16.
 #ifndef LOCO_CQ_UNROLL_BF16
