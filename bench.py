@@ -259,7 +259,7 @@ def main():
                          "counters now runs on every call")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (peers are simulated "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (peers are simulated "
               "in memory); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
