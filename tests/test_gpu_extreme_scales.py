@@ -191,3 +191,49 @@ def test_sa_extreme_scales(gpu_lib, bits, od):
         assert_f32_nan_aware(host(out.t), want, f"bits={bits}")
     else:
         assert_bf16_nan_aware(bf16_bits(out.t), want, f"bits={bits}")
+
+
+@pytest.mark.parametrize("adam", [False, True])
+def test_extreme_scale_in_a_late_peer_group(gpu_lib, adam):
+    """40 peers: the steps of a tile are computed for one group of peers at a time (16 peers
+    per group for the bf16 shard, 32 for the fused Adam step), so a tile whose only extreme
+    scales sit in the last group has accumulated the earlier groups when it switches to the
+    element-wise path; that path must start the tile over."""
+    n, bits, block, npeers = 50_000 + 123, 4, 256, 40
+    nb = -(-n // block)
+    say(f"extreme scale in the last peer group ({'fused Adam' if adam else 'bf16 out'})")
+    pays = []
+    for p in range(npeers):
+        codes, a = W.random_payload(n, bits, block, key=("late-group", adam, p))
+        if p >= 32:
+            a = torch.from_numpy(extreme_absmax(nb, bits, W.seed_of("late-group-absmax", adam, p) % 2 ** 32,
+                                                region=4))
+        pays.append((codes, a))
+    hp = dict(lr=1e-4, beta1=0.1, beta2=0.01, delta=1e-8)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        if adam:
+            rng = np.random.default_rng(5)
+            theta0 = rng.standard_normal(n).astype(np.float32) * 0.02
+            th = Guarded(n, torch.float32, init=torch.from_numpy(theta0))
+            m = Guarded(n, torch.float32, init=torch.zeros(n))
+            v = Guarded(n, torch.float32, init=torch.zeros(n))
+            gpu_lib.loco_dequant_reduce_adam([(c.cuda(), a.cuda()) for c, a in pays], n, bits=bits, block=block,
+                                             out_scale=1.0 / npeers, param=th.t, m=m.t, v=v.t, **hp)
+            torch.cuda.synchronize()
+            ref = oracle.dequant_reduce_adam([(c.numpy(), a.numpy()) for c, a in pays], n, bits=bits, block=block,
+                                             out_scale=1.0 / npeers, theta=theta0, m=np.zeros(n, np.float32),
+                                             v=np.zeros(n, np.float32), **hp)
+            assert_f32_nan_aware(host(m.t), ref["m"], "m")
+            assert_f32_nan_aware(host(v.t), ref["v"], "v")
+            assert_f32_nan_aware(host(th.t), ref["theta"], "theta")
+            for b, nm in ((th, "theta"), (m, "m"), (v, "v")):
+                b.check(nm)
+        else:
+            out = Guarded(n, torch.bfloat16)
+            gpu_lib.loco_dequant_reduce([(c.cuda(), a.cuda()) for c, a in pays], n, bits=bits, block=block,
+                                        out=out.t, out_scale=1.0 / npeers)
+            torch.cuda.synchronize()
+            want = oracle.dequant_reduce([(c.numpy(), a.numpy()) for c, a in pays], n, bits=bits, block=block,
+                                         out_scale=1.0 / npeers, out_dtype="bf16")
+            out.check("out")
+            assert_bf16_nan_aware(bf16_bits(out.t), want, "out")
