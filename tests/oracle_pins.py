@@ -304,6 +304,22 @@ def pin_dequant_huge_scales(O):
     assert np.all(np.isfinite(got)) and np.all(got == F32(7) * (fmax[0] / F32(7)))
 
 
+def pin_dequant_reduce_peer_order(O):
+    """Eqn. (8) sums the peers' decompressed values in peer order, rounding after each add:
+    with d = 1, 2^-24, -1 (4-bit codes 1, 1, -1 at steps 1, 2^-24, 1) the fp32 sum is
+    (1 + 2^-24) - 1 = 0, since 1 + 2^-24 is a tie that rounds to 1; in the reverse order it
+    would be (-1 + 2^-24) + 1 = 2^-24."""
+    one = np.array([0x01], np.uint8)          # codes +1, 0
+    neg = np.array([0x0F], np.uint8)          # codes -1, 0
+    p0 = (one, np.array([7.0], F32))          # step 1
+    p1 = (one, np.array([7 * 2.0 ** -24], F32))  # step 2^-24
+    p2 = (neg, np.array([7.0], F32))          # step 1
+    got = O.dequant_reduce([p0, p1, p2], 2, bits=4, block=2, out_scale=1.0)
+    assert np.array_equal(got.view(np.uint32), np.zeros(2, F32).view(np.uint32)), got
+    got = O.dequant_reduce([p2, p1, p0], 2, bits=4, block=2, out_scale=1.0)
+    assert np.array_equal(got, np.array([2.0 ** -24, 0.0], F32)), got
+
+
 # -- P-11: all-zero blocks ---------------------------------------------------------------------
 
 def pin_zero_blocks(O):
@@ -804,4 +820,5 @@ ALL_PINS = [
     pin_sa_worked, pin_sa_brute_force, pin_sa_dense_equivalent, pin_sa_transmits_topk,
     pin_adam_worked, pin_adam_closed_form, pin_adam_limits, pin_cq_scalar_twin, pin_dr_scalar_twin,
     pin_dra_worked, pin_tiny_scales, pin_topk_tiny_scales, pin_dequant_huge_scales,
+    pin_dequant_reduce_peer_order,
 ]

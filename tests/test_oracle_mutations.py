@@ -212,6 +212,10 @@ def _dequant_offset_form(q, step_per_elem):
     return (q + 8).astype(step_per_elem.dtype) * step_per_elem - ft(8) * step_per_elem
 
 
+def _dr_reversed(payloads, n, **kw):
+    return _orig["dequant_reduce"](list(reversed(payloads)), n, **kw)
+
+
 MUTATIONS = {
     "error_update drops beta*e": ("error_update", _drop_beta_term),
     "error_update swaps beta and 1-beta": ("error_update", _swap_weights),
@@ -243,6 +247,7 @@ MUTATIONS = {
     "tiny block keeps an infinite reciprocal": ("finite_reciprocal", _recip_keeps_overflow),
     "reciprocal zeroed for every subnormal step": ("finite_reciprocal", _recip_zero_subnormal),
     "decompressor as a biased product minus its offset": ("dequantize", _dequant_offset_form),
+    "dequant-reduce in reversed peer order": ("dequant_reduce", _dr_reversed),
 }
 
 
