@@ -216,6 +216,56 @@ def _dr_reversed(payloads, n, **kw):
     return _orig["dequant_reduce"](list(reversed(payloads)), n, **kw)
 
 
+def _tk_variant(bug):
+    """topk_quantize with one planted mistake (written out here, the oracle untouched)."""
+    def tk(g, e, *, chunk, k, bits=2, decay=1.0, ftype=np.float32):
+        g = np.asarray(g, dtype=ftype)
+        e = np.asarray(e, dtype=ftype)
+        h = ftype(decay) * g + e if bug == "decay on g" else g + ftype(decay) * e
+        n = h.size
+        nchunks = -(-n // chunk)
+        cbytes = -(-k * bits // 8)
+        qmax = O.qmax_of(bits)
+        idx_out = np.full((nchunks, k), 0xFFFF, dtype=np.uint16)
+        codes_out = np.zeros((nchunks, cbytes), dtype=np.uint8)
+        absmax_out = np.zeros(nchunks, dtype=ftype)
+        e_new = h.copy()
+        for c in range(nchunks):
+            lo, hi = c * chunk, min(n, (c + 1) * chunk)
+            hc = h[lo:hi]
+            keff = min(k, hi - lo)
+            src = g[lo:hi] if bug == "select by g" else hc
+            key = np.abs(src.astype(np.float32)).view(np.uint32)
+            sel = O.topk_order_select(key, keff)
+            vals = hc[sel]
+            absmax = np.max(np.abs(vals))
+            step = absmax / ftype(qmax)
+            inv = O.finite_reciprocal(np.array([step], dtype=ftype))[0]
+            q = np.clip(np.rint(vals * inv), -(qmax + 1), qmax).astype(np.int64)
+            d = q.astype(ftype) * step
+            e_new[lo + sel] = vals if bug == "kept error not reduced" else vals - d
+            if bug == "unselected error zeroed":
+                rest = np.ones(hi - lo, bool)
+                rest[sel] = False
+                e_new[lo:hi][rest] = 0
+            idx_out[c, :keff] = sel.astype(np.uint16)
+            codes_out[c] = O.pack_codes(np.concatenate([q, np.zeros(k - keff, np.int64)]), bits)
+            absmax_out[c] = absmax
+        return {"idx": idx_out.reshape(-1), "codes": codes_out.reshape(-1),
+                "absmax": absmax_out, "e_new": e_new, "h": h}
+    return tk
+
+
+def _adam_v_linear(theta, m, v, g, *, lr, beta1, beta2, delta, ftype=np.float32):
+    ft = ftype
+    theta, m, v, g = (np.asarray(x, dtype=ft) for x in (theta, m, v, g))
+    b1, b2 = ft(beta1), ft(beta2)
+    m_new = (ft(1) - b1) * m + b1 * g
+    v_new = (ft(1) - b2) * v + b2 * np.abs(g)
+    u = ft(1) / np.sqrt(v_new + ft(delta))
+    return theta - ft(lr) * (m_new * u), m_new, v_new
+
+
 MUTATIONS = {
     "error_update drops beta*e": ("error_update", _drop_beta_term),
     "error_update swaps beta and 1-beta": ("error_update", _swap_weights),
@@ -248,6 +298,11 @@ MUTATIONS = {
     "reciprocal zeroed for every subnormal step": ("finite_reciprocal", _recip_zero_subnormal),
     "decompressor as a biased product minus its offset": ("dequantize", _dequant_offset_form),
     "dequant-reduce in reversed peer order": ("dequant_reduce", _dr_reversed),
+    "top-k decay applied to g instead of e": ("topk_quantize", _tk_variant("decay on g")),
+    "top-k selects by |g| instead of |h|": ("topk_quantize", _tk_variant("select by g")),
+    "top-k keeps h as the error of the sent values": ("topk_quantize", _tk_variant("kept error not reduced")),
+    "top-k zeroes the error of the unsent values": ("topk_quantize", _tk_variant("unselected error zeroed")),
+    "Adam second moment of |g| instead of g^2": ("adam_step", _adam_v_linear),
 }
 
 
