@@ -371,11 +371,11 @@ __device__ __forceinline__ int find_segment(const CqParams& p, int64_t t) {
 // One wave tile per wave: tile tbase + (the wave's index in the launch).  Nothing is
 // carried from tile to tile (33 VGPRs for the 7B shard's kernel, 50 with an 8-bit error).
 template <int GK, int EK, int BITS, int B, bool FIXED>
-__global__ __launch_bounds__(kCqThreads) void cq_kernel(CqParams p, int64_t tbase) {
+__global__ __launch_bounds__(cq_threads(EK)) void cq_kernel(CqParams p, int64_t tbase) {
     const int lane = lane_id();
     constexpr int TILE = cq_tile_elems(EK);
     const int64_t wg = xcd_remap<kXcds, cq_xcd_run(EK)>(blockIdx.x, gridDim.x);
-    const int64_t t = tbase + wg * (kCqThreads / kWave) + uniform(threadIdx.x / kWave);
+    const int64_t t = tbase + wg * (cq_threads(EK) / kWave) + uniform(threadIdx.x / kWave);
     if (t >= p.ntiles) return;
     const CqSegDev sg = p.seg[find_segment(p, t)];
     const int64_t base = (t - sg.tile0) * TILE;
@@ -439,13 +439,14 @@ hipError_t launch_cq(const CqParams& p, int grad_kind, int err_kind, int bits, i
     else if (grad_kind == kF32) k = pick_err<kF32>(err_kind, fixed, bits, block);
     if (!k) return hipErrorInvalidValue;
     // one wave per tile; launches of at most kMaxGrid workgroups
-    const int64_t waves_per_block = kCqThreads / kWave;
+    const int threads = cq_threads(err_kind);
+    const int64_t waves_per_block = threads / kWave;
     const int64_t per_launch = kMaxGrid * waves_per_block;
     for (int64_t tbase = 0; tbase < p.ntiles; tbase += per_launch) {
         const int64_t tiles = p.ntiles - tbase < per_launch ? p.ntiles - tbase : per_launch;
         const int64_t blocks = (tiles + waves_per_block - 1) / waves_per_block;
         void* args[] = {(void*)&p, (void*)&tbase};
-        const hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(kCqThreads), args, 0, stream);
+        const hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;

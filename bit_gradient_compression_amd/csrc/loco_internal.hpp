@@ -35,8 +35,17 @@ namespace loco {
 #ifndef LOCO_CQ_XCD_RUN_BF16
 #define LOCO_CQ_XCD_RUN_BF16 32
 #endif
+// Workgroup size and XCD run per error kind, with runs of 128 waves in each case.  An fp32
+// error takes one-wave workgroups in runs of 128, an 8-bit error two-wave workgroups in
+// runs of 64, a bf16 error four-wave workgroups in runs of 32.  Measured on MI355X (back
+// to back / flushed, ms): 7B shard 1.389 / 1.387 against 1.403-1.412 / 1.403 with 4-wave
+// workgroups; LLaMA layer 0.329 / 0.327 against 0.335 / 0.335; 8-bit error 0.612 / 0.614
+// against 0.629 / 0.620.  The MoE experts (bf16 error) are slower with smaller workgroups
+// (1.46-1.56 against 1.43-1.44).  Other mixes (64-thread workgroups in runs of 64 or 256;
+// 128-thread ones in runs of 64 for the fp32 error; one-wave ones for the 8-bit error)
+// fall between these and the old default.
 #ifndef LOCO_CQ_THREADS
-#define LOCO_CQ_THREADS 256
+#define LOCO_CQ_THREADS 64
 #endif
 #ifndef LOCO_DR_UNROLL
 #define LOCO_DR_UNROLL 2
@@ -50,7 +59,7 @@ namespace loco {
 #define LOCO_TK_WAVES_PER_EU 6
 #endif
 #ifndef LOCO_CQ_XCD_RUN
-#define LOCO_CQ_XCD_RUN 32
+#define LOCO_CQ_XCD_RUN 128
 #endif
 #ifndef LOCO_SA_XCD_RUN
 #define LOCO_SA_XCD_RUN 64
@@ -89,6 +98,18 @@ constexpr int cq_unroll(int err_kind) {
 }
 constexpr int cq_tile_elems(int err_kind) { return 64 * kCqVec * cq_unroll(err_kind); }  // per wave tile
 constexpr int kCqThreads = LOCO_CQ_THREADS;
+// Workgroup size per error kind (threads; a multiple of 64).
+#ifndef LOCO_CQ_THREADS_I8
+#define LOCO_CQ_THREADS_I8 128
+#endif
+#ifndef LOCO_CQ_THREADS_BF16
+#define LOCO_CQ_THREADS_BF16 256
+#endif
+constexpr int kCqThreadsI8 = LOCO_CQ_THREADS_I8;
+constexpr int kCqThreadsBf16 = LOCO_CQ_THREADS_BF16;
+constexpr int cq_threads(int err_kind) {
+    return err_kind == 2 ? kCqThreadsI8 : err_kind == 1 ? kCqThreadsBf16 : kCqThreads;
+}
 
 struct CqSegDev {
     const void* g;

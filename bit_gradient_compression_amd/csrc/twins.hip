@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kThreads) void twin_copy_kernel(const u32x4* src, u
 // count, block b's absmax.  The lane layout is the kernel's: two pieces of 4 elements at
 // 4l and 256 + 4l when the gradient or the error is fp32 (each instruction then covers a
 // contiguous run), else 8 consecutive elements at 8l.  U sub-tiles of 512 elements per
-// wave; workgroups renumbered in XCD runs.
+// wave; the kernel's workgroup size per error kind, workgroups renumbered in XCD runs.
 
 template <int N>
 struct Raw {
@@ -68,15 +68,15 @@ __device__ __forceinline__ void stnt(void* p, const uint32_t* w) {
     else __builtin_nontemporal_store((uint8_t)w[0], (uint8_t*)p);
 }
 
-template <int GB, int EB, int BITS, int U, int RUN>
-__global__ __launch_bounds__(kThreads) void twin_cq_kernel(const void* g, void* e, uint8_t* codes, float* absmax,
-                                                           int64_t ntiles, int nb) {
+template <int GB, int EB, int BITS, int U, int RUN, int TPB>
+__global__ __launch_bounds__(TPB) void twin_cq_kernel(const void* g, void* e, uint8_t* codes, float* absmax,
+                                                      int64_t ntiles, int nb) {
     constexpr bool SPLIT = GB == 4 || EB == 4;
     constexpr int N = SPLIT ? 4 : 8;  // elements per access
     constexpr int PIECES = 8 / N;
     const int lane = lane_id();
     const int64_t wg = xcd_remap<8, RUN>(blockIdx.x, gridDim.x);
-    const int64_t t = wg * (kThreads / 64) + uniform(threadIdx.x / 64);
+    const int64_t t = wg * (TPB / 64) + uniform(threadIdx.x / 64);
     if (t >= ntiles) return;
     Raw<(N * GB + 3) / 4> gw[U][PIECES];
     Raw<(N * EB + 3) / 4> ew[U][PIECES];
@@ -283,18 +283,22 @@ __attribute__((visibility("default"))) int loco_twin_cq(const void* g, void* e, 
     if (ntiles <= 0 || block < 64 || block > 512 || (block & (block - 1)) != 0) return -1;
     const int nb = 512 * U / block;
     const void* k = nullptr;
-#define LOCO_TWIN_CQ(GB, EK, EB, BI, UU, RUN) \
-    if (gbytes == GB && ekind == EK && bits == BI) k = (const void*)&twin_cq_kernel<GB, EB, BI, UU, RUN>;
-    LOCO_TWIN_CQ(2, 0, 4, 4, 1, 32)
-    LOCO_TWIN_CQ(2, 0, 4, 8, 1, 32)
-    LOCO_TWIN_CQ(2, 1, 2, 4, 1, 32)
-    LOCO_TWIN_CQ(2, 2, 1, 4, 2, 64)
-    LOCO_TWIN_CQ(4, 0, 4, 4, 1, 32)
+    int tpb = 0;
+    // the kernel's workgroup size and XCD run per error kind
+#define LOCO_TWIN_CQ(GB, EK, EB, BI, UU, RUN, TPB)                                       \
+    if (gbytes == GB && ekind == EK && bits == BI) {                                      \
+        k = (const void*)&twin_cq_kernel<GB, EB, BI, UU, RUN, TPB>;                       \
+        tpb = TPB;                                                                        \
+    }
+    LOCO_TWIN_CQ(2, 0, 4, 4, 1, 128, 64)
+    LOCO_TWIN_CQ(2, 0, 4, 8, 1, 128, 64)
+    LOCO_TWIN_CQ(2, 1, 2, 4, 1, 32, 256)
+    LOCO_TWIN_CQ(2, 2, 1, 4, 2, 64, 128)
+    LOCO_TWIN_CQ(4, 0, 4, 4, 1, 128, 64)
 #undef LOCO_TWIN_CQ
     if (!k) return -1;
     void* args[] = {(void*)&g, (void*)&e, (void*)&codes, (void*)&absmax, (void*)&ntiles, (void*)&nb};
-    return hipLaunchKernel(k, dim3((unsigned)grid_of(ntiles, kThreads / 64)), dim3(kThreads), args, 0,
-                           (hipStream_t)stream);
+    return hipLaunchKernel(k, dim3((unsigned)grid_of(ntiles, tpb / 64)), dim3(tpb), args, 0, (hipStream_t)stream);
 }
 
 // 8 peers of 4-bit codes; mode 0: fp32 out, 1: bf16 out, 2: Adam step on theta, m, v (+ the
