@@ -201,7 +201,7 @@ __device__ __forceinline__ void store4f(float* dst, int64_t i0, const float* x) 
 constexpr int dr_waves_per_eu(int mode) { return mode == kDrOutAdam ? LOCO_DRA_WAVES_PER_EU : 1; }
 
 template <int BITS, int B, bool FIXED, int MODE>
-__global__ __launch_bounds__(kDrThreads) __attribute__((amdgpu_waves_per_eu(dr_waves_per_eu(MODE))))
+__global__ __launch_bounds__(dr_threads(MODE)) __attribute__((amdgpu_waves_per_eu(dr_waves_per_eu(MODE))))
 void dr_kernel(DrParams p, int64_t tbase) {
     using LY = DrLayout<MODE>;
     constexpr bool SPLIT = LY::kSplit;
@@ -211,14 +211,14 @@ void dr_kernel(DrParams p, int64_t tbase) {
     static_assert(TILE % B == 0, "a wave tile spans whole scale blocks");
     constexpr int SUB = 64 * kDrVec;
     const int lane = lane_id();
-    const int64_t wg = xcd_remap<kXcds, kDrXcdRun>(blockIdx.x, gridDim.x);
+    const int64_t wg = xcd_remap<kXcds, dr_xcd_run(MODE)>(blockIdx.x, gridDim.x);
     // element offsets, within the tile, of the lane's pieces in each sub-tile
     int pos[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int pc = 0; pc < 2; ++pc) pos[u][pc] = u * SUB + LY::piece(lane, pc);
-    const int64_t t = tbase + wg * (kDrThreads / kWave) + uniform(threadIdx.x / kWave);
+    const int64_t t = tbase + wg * (dr_threads(MODE) / kWave) + uniform(threadIdx.x / kWave);
     if (t >= p.ntiles) return;
     {
         const int64_t tb = t * TILE;  // the tile's first element
@@ -479,13 +479,14 @@ hipError_t launch_dr(const DrParams& p, int bits, int block, bool fixed, int mod
     }
     if (!k) return hipErrorInvalidValue;
     // one wave per tile; launches of at most kMaxGrid workgroups
-    const int64_t waves_per_block = kDrThreads / kWave;
+    const int threads = dr_threads(mode);
+    const int64_t waves_per_block = threads / kWave;
     const int64_t per_launch = kMaxGrid * waves_per_block;
     for (int64_t tbase = 0; tbase < p.ntiles; tbase += per_launch) {
         const int64_t tiles = p.ntiles - tbase < per_launch ? p.ntiles - tbase : per_launch;
         const int64_t blocks = (tiles + waves_per_block - 1) / waves_per_block;
         void* args[] = {(void*)&p, (void*)&tbase};
-        const hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(kDrThreads), args, 0, stream);
+        const hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;

@@ -140,8 +140,21 @@ constexpr int kDrMaxPeers = 128;
 constexpr int kDrVec = 8;                          // consecutive outputs per lane per sub-tile
 constexpr int kDrUnroll = LOCO_DR_UNROLL;          // sub-tiles per wave tile
 constexpr int kDrThreads = LOCO_DR_THREADS;
+// The fused Adam step: one-wave workgroups in XCD runs of 64 (0.527-0.529 / 0.526-0.528 ms
+// back to back / flushed on 8 peers x 105,250,000, against 0.531-0.533 / 0.536-0.538
+// with the shard's 4-wave workgroups in runs of 16; the bf16 shard is within noise of its
+// default with either).
+#ifndef LOCO_DRA_THREADS
+#define LOCO_DRA_THREADS 64
+#endif
+#ifndef LOCO_DRA_XCD_RUN
+#define LOCO_DRA_XCD_RUN 64
+#endif
+
 // Output modes: the reduced shard as fp32 or bf16, or the fused Adam-family step.
 enum : int { kDrOutF32 = 0, kDrOutBf16 = 1, kDrOutAdam = 2 };
+constexpr int dr_threads(int mode) { return mode == kDrOutAdam ? LOCO_DRA_THREADS : kDrThreads; }
+constexpr int dr_xcd_run(int mode) { return mode == kDrOutAdam ? LOCO_DRA_XCD_RUN : LOCO_DR_XCD_RUN; }
 // The fused step holds theta, m and v of each sub-tile in registers as well, so its waves
 // take one sub-tile.
 #ifndef LOCO_DRA_UNROLL

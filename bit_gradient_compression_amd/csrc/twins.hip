@@ -117,13 +117,18 @@ struct TwinPeers {
     const float* absmax[kTwinMaxPeers];
 };
 
+// The kernel's workgroup shape per mode: 4-wave workgroups in XCD runs of 16 for a shard,
+// one-wave workgroups in runs of 64 for the Adam step.
+constexpr int twin_dr_tpb(int mode) { return mode == 2 ? 64 : 256; }
+constexpr int twin_dr_run(int mode) { return mode == 2 ? 64 : 16; }
+
 template <int BITS, int MODE, int U, int P>
-__global__ __launch_bounds__(kThreads) void twin_dr_kernel(TwinPeers pp, int64_t ntiles, int lb, void* out,
-                                                           float* theta, float* m, float* v, uint16_t* tb) {
+__global__ __launch_bounds__(twin_dr_tpb(MODE)) void twin_dr_kernel(TwinPeers pp, int64_t ntiles, int lb, void* out,
+                                                                    float* theta, float* m, float* v, uint16_t* tb) {
     constexpr bool SPLIT = MODE != 1;
     const int lane = lane_id();
-    const int64_t wg = xcd_remap<8, 16>(blockIdx.x, gridDim.x);
-    const int64_t t = wg * (kThreads / 64) + uniform(threadIdx.x / 64);
+    const int64_t wg = xcd_remap<8, twin_dr_run(MODE)>(blockIdx.x, gridDim.x);
+    const int64_t t = wg * (twin_dr_tpb(MODE) / 64) + uniform(threadIdx.x / 64);
     if (t >= ntiles) return;
     auto at = [&](int u, int pc) { return (t * U + u) * 512 + (SPLIT ? pc * 256 + lane * 4 : lane * 8 + pc * 4); };
     f32x4 th[U][2], mo[U][2], ve[U][2];
@@ -322,8 +327,8 @@ __attribute__((visibility("default"))) int loco_twin_dr(const uint8_t* const* co
                               : (const void*)&twin_dr_kernel<4, 2, 1, 8>;
     void* args[] = {(void*)&pp, (void*)&ntiles, (void*)&lb, (void*)&out, (void*)&theta, (void*)&m, (void*)&v,
                     (void*)&tb};
-    return hipLaunchKernel(k, dim3((unsigned)grid_of(ntiles, kThreads / 64)), dim3(kThreads), args, 0,
-                           (hipStream_t)stream);
+    const int tpb = mode == 2 ? twin_dr_tpb(2) : twin_dr_tpb(0);
+    return hipLaunchKernel(k, dim3((unsigned)grid_of(ntiles, tpb / 64)), dim3(tpb), args, 0, (hipStream_t)stream);
 }
 
 __attribute__((visibility("default"))) int loco_twin_tk(const float* g, float* e, uint16_t* idx, uint8_t* codes,
