@@ -71,9 +71,8 @@ constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 // Workgroups are dispatched round-robin over the chip's 8 XCDs (each with its own L2).
 // The streaming kernels renumber their workgroups so that runs of consecutive logical
 // workgroups execute on one XCD (1: identity).  Measured on MI355X for compensate-
-// quantize: runs of ~128 waves (32 workgroups of 256 threads) per XCD move the fused
-// kernel from ~68% to ~71.5% of peak HBM bandwidth; short runs (16-32 waves) are slower
-// than the identity.
+// quantize: runs of ~128 waves per XCD moved the fused kernel from ~68% to ~71.5% of peak
+// HBM bandwidth; short runs (16-32 waves) are slower than the identity.
 constexpr int kXcds = 8;
 constexpr int kCqXcdRun = LOCO_CQ_XCD_RUN;
 constexpr int kCqXcdRunI8 = LOCO_CQ_XCD_RUN_I8;
