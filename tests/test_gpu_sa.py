@@ -105,8 +105,10 @@ def test_sa_deterministic(gpu_lib):
 
 @pytest.mark.parametrize("od", ["f32", "bf16"])
 def test_sa_many_chunks_per_workgroup(gpu_lib, od):
-    """More chunks than the persistent grid has workgroups, so each walks several (its
-    next payload loaded while the current chunk is applied), plus a short last chunk."""
+    """6,000 chunks and a short last one.  bf16 output: more chunks than the persistent
+    grid has workgroups, so each walks several (its next payload loaded while the current
+    chunk is applied).  fp32 output: the general kernel, one workgroup per chunk, after the
+    pre-read of all the payloads."""
     chunk, k = 256, 82
     n = chunk * 6000 + 37
     say(f"sa many chunks per workgroup, n={n}, {od}")
