@@ -358,12 +358,15 @@ __global__ __launch_bounds__(NT) void sa_stream_kernel(SaParams p) {
 // exposed, one workgroup per chunk hides it once the payloads are in the caches.
 template <int C, int BITS>
 void pick_out(bool out_bf16, bool stream, const void*& k) {
-    if (stream)
-        k = out_bf16 ? (const void*)&sa_stream_kernel<C, BITS, true, kSaThreadsBf16>
-                     : (const void*)&sa_stream_kernel<C, BITS, false, kSaThreadsF32>;
-    else
+    // (the streaming kernel is built for an output type only where its setting takes it)
+    if (stream && out_bf16) {
+        if constexpr (kSaWgPerCuBf16 > 0) k = (const void*)&sa_stream_kernel<C, BITS, true, kSaThreadsBf16>;
+    } else if (stream) {
+        if constexpr (kSaWgPerCuF32 > 0) k = (const void*)&sa_stream_kernel<C, BITS, false, kSaThreadsF32>;
+    } else {
         k = out_bf16 ? (const void*)&sa_kernel<C, BITS, true, kSaThreadsBf16>
                      : (const void*)&sa_kernel<C, BITS, false, kSaThreadsF32>;
+    }
 }
 
 template <int C>
