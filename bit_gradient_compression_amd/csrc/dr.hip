@@ -57,9 +57,10 @@ __device__ __forceinline__ int code_of(u32x2 w, int j) {
 // exact value is q*step, rounded once, so the result is bit-identical to rounding q*step
 // (2^(b-1)*step is exact).  1: c enters the fma as a binary16 subnormal, c * 2^-24, taken
 // straight from the low or high half of a word of masked codes by the mixed-precision fma
-// (v_fma_mix_f32), against a step scaled by 2^24 (exact): per code one masked half-word
-// (two codes per mask), one fma, one add.  0: c is converted with the byte converts
-// (v_cvt_f32_ubyteN), one more instruction per code.
+// (v_fma_mix_f32), against a step scaled by 2^24 (exact); a 4-bit code masked at bits 4-7
+// of a half reads as 16c * 2^-24 and meets the step scaled by 2^20.  Per code: 5/8 (4-bit)
+// or 3/4 (8-bit) of a bias-mask-shift instruction, one fma, one add.  0: c is converted
+// with the byte converts (v_cvt_f32_ubyteN).
 #ifndef LOCO_DR_DECODE_F16
 #define LOCO_DR_DECODE_F16 1
 #endif
@@ -84,20 +85,31 @@ __device__ __forceinline__ void acc_byte(float& a, uint32_t x, float step, float
 // w.x holds codes 0-3 in its low and 4-7 in its high 16 bits at 4 bits (2 bits: low and
 // high byte); at 8 bits w.x holds codes 0-3 and w.y codes 4-7.
 // 2 bits: acc + (float)q * step.  4 and 8 bits: s is step * 2^24 (LOCO_DR_DECODE_F16) or
-// step, o = -2^(b-1) * step, with |step| < 2^100 so that neither overflows.
+// step, o = -2^(b-1) * step, with |step| < 2^100 so that neither overflows; s16 (4 bits,
+// LOCO_DR_DECODE_F16) is step * 2^20, for the codes held at bits 4-7 of a half.
 template <int BITS>
-__device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float sa, float oa, float sb, float ob) {
+__device__ __forceinline__ void accumulate8(float (&acc)[kDrVec], u32x2 w, float sa, float oa, float sb, float ob,
+                                            float sa16, float sb16) {
     if constexpr (BITS == 2) {
 #pragma unroll
         for (int j = 0; j < kDrVec; ++j) acc[j] = acc[j] + (float)code_of<BITS>(w, j) * (j < 4 ? sa : sb);
     } else if constexpr (kDecodeF16 && BITS == 4) {
-        const uint32_t x = w.x ^ 0x88888888u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t c = (x >> (4 * j)) & 0x000F000Fu;  // codes j and j + 4
-            acc[j] = acc[j] + __builtin_fmaf(half_lo(c), sa, oa);
-            acc[j + 4] = acc[j + 4] + __builtin_fmaf(half_hi(c), sb, ob);
-        }
+        // Codes j and j + 4 sit in nibble j of the low and the high half.  Nibbles 0 and
+        // 1 of each half are masked in place (nibble 1 reads as 16c * 2^-24, against
+        // s16); one shift brings nibbles 2 and 3 down to the same places: 5 instructions
+        // (4 xor-and, 1 shift) bias and mask 8 codes, where shifting every nibble down
+        // took 8.
+        const uint32_t y = w.x >> 8;
+        const uint32_t c04 = (w.x ^ 0x88888888u) & 0x000F000Fu, c15 = (w.x ^ 0x88888888u) & 0x00F000F0u;
+        const uint32_t c26 = (y ^ 0x88888888u) & 0x000F000Fu, c37 = (y ^ 0x88888888u) & 0x00F000F0u;
+        acc[0] = acc[0] + __builtin_fmaf(half_lo(c04), sa, oa);
+        acc[1] = acc[1] + __builtin_fmaf(half_lo(c15), sa16, oa);
+        acc[2] = acc[2] + __builtin_fmaf(half_lo(c26), sa, oa);
+        acc[3] = acc[3] + __builtin_fmaf(half_lo(c37), sa16, oa);
+        acc[4] = acc[4] + __builtin_fmaf(half_hi(c04), sb, ob);
+        acc[5] = acc[5] + __builtin_fmaf(half_hi(c15), sb16, ob);
+        acc[6] = acc[6] + __builtin_fmaf(half_hi(c26), sb, ob);
+        acc[7] = acc[7] + __builtin_fmaf(half_hi(c37), sb16, ob);
     } else if constexpr (kDecodeF16 && BITS == 8) {
         const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
         const uint32_t c02 = x0 & 0x00FF00FFu, c13 = (x0 >> 8) & 0x00FF00FFu;
@@ -310,8 +322,11 @@ void dr_kernel(DrParams p, int64_t tbase) {
                         break;
                     }
                 }
-                // the decoder's scale, and its offset -2^(b-1)*step (exact), once per scale
+                // the decoder's scales (4 bits: also step * 2^20, for upper nibbles) and its
+                // offset -2^(b-1)*step, all exact, once per scale
                 const float scl = (BITS != 2 && kDecodeF16) ? stp * kF16SubScale : stp;
+                constexpr bool S16 = BITS == 4 && kDecodeF16;
+                const float scl16 = S16 ? stp * (kF16SubScale / 16.0f) : scl;
                 const float offp = -(float)(1 << (BITS - 1)) * stp;
                 for (int q0 = 0; q0 < ng; q0 += kDrPeerBatch) {
                     if (q0 > 0) load_batch(q0);
@@ -329,26 +344,27 @@ void dr_kernel(DrParams p, int64_t tbase) {
                         if (q0 + b < ng) {
 #pragma unroll
                             for (int u = 0; u < U; ++u) {
-                                float sa = scl, oa = offp, sb = scl, ob = offp;
+                                float sa = scl, oa = offp, sb = scl, ob = offp, sa16 = scl16, sb16 = scl16;
                                 if constexpr (!FIXED) {
+                                    auto fetch = [](int addr, float x) {
+                                        return __builtin_bit_cast(
+                                            float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
+                                    };
                                     const int a0 = src[u][0] + b * BPT * 4;
-                                    sa = __builtin_bit_cast(
-                                        float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, scl)));
-                                    if constexpr (BITS != 2)
-                                        oa = __builtin_bit_cast(
-                                            float, __builtin_amdgcn_ds_bpermute(a0, __builtin_bit_cast(int, offp)));
+                                    sa = fetch(a0, scl);
+                                    if constexpr (BITS != 2) oa = fetch(a0, offp);
+                                    if constexpr (S16) sa16 = fetch(a0, scl16);
                                     sb = sa;
                                     ob = oa;
+                                    sb16 = sa16;
                                     if constexpr (TWO) {
                                         const int a1 = src[u][1] + b * BPT * 4;
-                                        sb = __builtin_bit_cast(
-                                            float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, scl)));
-                                        if constexpr (BITS != 2)
-                                            ob = __builtin_bit_cast(
-                                                float, __builtin_amdgcn_ds_bpermute(a1, __builtin_bit_cast(int, offp)));
+                                        sb = fetch(a1, scl);
+                                        if constexpr (BITS != 2) ob = fetch(a1, offp);
+                                        if constexpr (S16) sb16 = fetch(a1, scl16);
                                     }
                                 }
-                                accumulate8<BITS>(acc[u], w[b][u], sa, oa, sb, ob);
+                                accumulate8<BITS>(acc[u], w[b][u], sa, oa, sb, ob, sa16, sb16);
                             }
                         }
                     }
