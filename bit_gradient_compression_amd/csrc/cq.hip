@@ -10,14 +10,16 @@
 // and a step may store e' = 0 instead (the periodic reset of Eqn. (7)).
 //
 // Mapping: a wavefront owns a tile of sub-tiles of 512 elements (one sub-tile with a
-// float error, two with an 8-bit error, whose waves move fewer bytes); lane l owns two
-// pieces of 4 consecutive elements of each sub-tile, at 4l and 256 + 4l, so that every
-// load and store instruction of the wave covers one contiguous run of memory (1 KB of an
-// fp32 error, 512 B of a bf16 gradient, 128 B of 4-bit codes).  The error is loaded and
-// stored non-temporally.  A scale block of B <= 256 elements is B/4 consecutive lanes of
-// one piece (a block of 512, both pieces of the wave); its absmax is reduced with DPP row
-// operations (and permlane swaps past 16 lanes).  Every load of a tile is issued before
-// any arithmetic.  The 8-bit-error kernel is bound by VALU issue as much as by
+// float error, two with an 8-bit error, whose waves move fewer bytes); lane l owns 8
+// elements of each sub-tile, as two pieces of 4 consecutive elements at 4l and 256 + 4l
+// where the gradient or the error is fp32, else as the 8 consecutive elements at 8l, so
+// that every load and store instruction of the wave covers one contiguous run of memory
+// (CqLayout).  The gradient and the error are loaded and the error stored non-temporally,
+// except where a tile's first or last line of a stream is shared with a neighbouring tile.
+// A scale block of B <= 256 elements is B/4 consecutive lanes of one piece (B/8 lanes of
+// consecutive elements; a block of 512, both pieces of the wave); its absmax is reduced
+// with DPP row operations (and permlane swaps past 16 lanes).  Every load of a tile is
+// issued before any arithmetic.  The 8-bit-error kernel is bound by VALU issue as much as by
 // HBM, so its per-element work is kept to a minimum: codes are packed from the float q
 // with v_cvt_pk_u8_f32, the int8 error is encoded by a magic-number add and v_perm, and
 // a wave issues the two divisions of its blocks once for all of its blocks (lane b
@@ -101,6 +103,84 @@ template <class T, bool NT>
 __device__ __forceinline__ T ld(const void* p) {
     if constexpr (NT) return __builtin_nontemporal_load((const T*)p);
     else return *(const T*)p;
+}
+
+constexpr int elem_bytes(int k) { return k == kI8 ? 1 : k == kBF16 ? 2 : 4; }
+
+// The N elements of kind K held in the words w (as loaded from memory) as floats.
+template <int K, int N>
+__device__ __forceinline__ void words_to_f32(u32x4 w, float* x, float estep, float eoff) {
+    if constexpr (K == kBF16) {
+        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+        if constexpr (N == 8) {
+            x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+        }
+    } else if constexpr (K == kI8) {
+        i8x4_to_f32(w.x, estep, eoff, x);
+        if constexpr (N == 8) i8x4_to_f32(w.y, estep, eoff, x + 4);
+    } else {
+        static_assert(N == 4, "fp32 elements come 4 at a time");
+        x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+        x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+    }
+}
+
+// The N * elem_bytes(K) bytes (4, 8 or 16) at byte offset off of a buffer resource, with
+// cache policy AUX (0: cached; kLoadNt: non-temporal).
+template <int K, int N, int AUX>
+__device__ __forceinline__ u32x4 load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    constexpr int BYTES = N * elem_bytes(K);
+    if constexpr (BYTES == 16) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    } else if constexpr (BYTES == 8) {
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+        return u32x4{w.x, w.y, 0u, 0u};
+    } else {
+        static_assert(BYTES == 4, "4, 8 or 16 bytes per lane");
+        return u32x4{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX), 0u, 0u, 0u};
+    }
+}
+
+// A segment need not start on a 128-byte line: then each stream's first and last line of
+// a wave tile also hold elements of the neighbouring tiles.  Accessed non-temporally, such
+// a line is fetched, and its halves written, separately for each of the two waves.  The
+// lanes whose bytes lie in such a line load them with the cached policy instead, so that
+// the two waves meet in L2; all other lanes load non-temporally.  Measured on the 7B
+// shard, whose partitions start 64 bytes into a line of the fp32 error: 1.0066 of the
+// algorithmic bytes and 1.365 ms, against 1.0118 and 1.380 ms with every load
+// non-temporal (partitions padded to start on a line: 0.9997 and 1.35-1.36 ms).  Most of
+// the time comes from the error's lines, whose writes then merge in L2.
+#ifndef LOCO_CQ_EDGE_CACHED
+#define LOCO_CQ_EDGE_CACHED 1
+#endif
+constexpr bool kEdgeCached = LOCO_CQ_EDGE_CACHED != 0;
+
+// N elements of kind K at element i0 of a full wave tile [t0, t1) of stream p, as loadn
+// with policy NT, except (EDGE) for the lanes in a shared edge line.  The loads go through
+// a buffer resource over the tile, whose cache policy is an immediate: two global loads of
+// one address that differ only in policy would be merged into one.
+template <int K, int N, bool NT>
+__device__ __forceinline__ void loadn(const void* p, int64_t i0, float* x, float estep, float eoff);
+
+template <int K, int N, bool NT, bool EDGE>
+__device__ __forceinline__ void loadn_tile(const void* p, int64_t t0, int64_t t1, int64_t i0, float* x,
+                                           float estep, float eoff) {
+    if constexpr (EDGE && NT) {
+        constexpr int64_t S = elem_bytes(K);
+        const char* tb = (const char*)p + t0 * S;  // wave-uniform
+        const uint32_t bytes = (uint32_t)((t1 - t0) * S);
+        const auto r = buffer_rsrc(tb, bytes);
+        // offsets, within the tile, of its first and last line boundaries
+        const uint32_t lo = (uint32_t)((128u - ((uintptr_t)tb & 127u)) & 127u);
+        const uint32_t hi = (uint32_t)((((uintptr_t)tb + bytes) & ~(uintptr_t)127) - (uintptr_t)tb);
+        const uint32_t off = (uint32_t)((i0 - t0) * S);
+        u32x4 w;
+        if (off < lo || off + (uint32_t)(N * S) > hi) w = load_words<K, N, 0>(r, off);
+        else w = load_words<K, N, kLoadNt>(r, off);
+        words_to_f32<K, N>(w, x, estep, eoff);
+    } else {
+        loadn<K, N, NT>(p, i0, x, estep, eoff);
+    }
 }
 
 // N = 4 or 8 consecutive elements starting at i0 (i0 a multiple of N).  NT: non-temporal.
@@ -191,6 +271,10 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
     float h[U][kCqVec];
     float e[U][kCqVec];
     const float eoff = -128.0f * p.err_step;  // the 8-bit error's decoder offset
+    // Not with an 8-bit error: that kernel is bound by instruction issue, and the edge
+    // lanes' extra instructions cost it more than the shared lines do (0.620 against 0.611
+    // ms back to back on the 7B shard).
+    constexpr bool EDGE = kEdgeCached && EK != kI8;
 
     // Issue every load of the tile first.
 #pragma unroll
@@ -198,15 +282,15 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
         float g[kCqVec];
         if constexpr (FULL && !SPLIT) {
             const int64_t i0 = base + u * SUB + LY::piece(lane, 0);
-            loadn<GK, 8, true>(sg.g, i0, g, 0.0f, 0.0f);
-            loadn<EK, 8, ENT>(sg.e, i0, e[u], p.err_step, eoff);
+            loadn_tile<GK, 8, true, EDGE>(sg.g, base, base + U * SUB, i0, g, 0.0f, 0.0f);
+            loadn_tile<EK, 8, ENT, EDGE>(sg.e, base, base + U * SUB, i0, e[u], p.err_step, eoff);
         } else {
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 const int64_t i0 = base + u * SUB + LY::piece(lane, pc);
                 if constexpr (FULL) {
-                    loadn<GK, 4, true>(sg.g, i0, g + 4 * pc, 0.0f, 0.0f);
-                    loadn<EK, 4, ENT>(sg.e, i0, e[u] + 4 * pc, p.err_step, eoff);
+                    loadn_tile<GK, 4, true, EDGE>(sg.g, base, base + U * SUB, i0, g + 4 * pc, 0.0f, 0.0f);
+                    loadn_tile<EK, 4, ENT, EDGE>(sg.e, base, base + U * SUB, i0, e[u] + 4 * pc, p.err_step, eoff);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {

@@ -26,14 +26,6 @@
 namespace loco {
 namespace {
 
-// A raw buffer resource over `bytes` bytes at p.  Loads through it take the base from
-// SGPRs and a 32-bit lane offset (no per-lane 64-bit address arithmetic), and an offset
-// past `bytes` reads 0 without touching memory.  Word 3 is gfx9's raw-buffer format.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-constexpr int kLoadNt = 2;  // cache-policy bit of a non-temporal (streaming) load on gfx950
-
 // Codes of N = 4 or 8 consecutive elements (N*BITS/8 bytes) at byte offset off of a
 // peer's tile, in the low bits.
 template <int BITS, int N>

@@ -104,6 +104,16 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t b0, uint32_t b1, uint32_
     return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
 }
 
+// ---- buffer resources ------------------------------------------------------------
+
+// A raw buffer resource over `bytes` bytes at p.  Loads through it take the base from
+// SGPRs and a 32-bit lane offset (no per-lane 64-bit address arithmetic), and an offset
+// past `bytes` reads 0 without touching memory.  Word 3 is gfx9's raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kLoadNt = 2;  // cache-policy bit of a non-temporal (streaming) load on gfx950
+
 // ---- wavefront primitives -------------------------------------------------------
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -12,7 +12,7 @@ namespace loco {
 
 // Launch shape of the streaming kernels.  The grid is not persistent: each wave takes one
 // tile and exits, so the waves in flight sweep memory in address order.  Past kMaxGrid
-// workgroups, compensate-quantize launches again; dequant-reduce grid-strides.
+// workgroups the launcher launches again, from the next tile.
 #ifndef LOCO_CQ_UNROLL
 #define LOCO_CQ_UNROLL 1
 #endif
