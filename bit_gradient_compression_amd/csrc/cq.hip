@@ -162,10 +162,16 @@ constexpr bool kEdgeCached = LOCO_CQ_EDGE_CACHED != 0;
 template <int K, int N, bool NT>
 __device__ __forceinline__ void loadn(const void* p, int64_t i0, float* x, float estep, float eoff);
 
+// head / tail: this load instruction's row holds the tile's first / last element (a
+// row in between has no shared edge line and loads as loadn does).
 template <int K, int N, bool NT, bool EDGE>
-__device__ __forceinline__ void loadn_tile(const void* p, int64_t t0, int64_t t1, int64_t i0, float* x,
-                                           float estep, float eoff) {
+__device__ __forceinline__ void loadn_tile(const void* p, int64_t t0, int64_t t1, int64_t i0, bool head, bool tail,
+                                           float* x, float estep, float eoff) {
     if constexpr (EDGE && NT) {
+        if (!head && !tail) {
+            loadn<K, N, NT>(p, i0, x, estep, eoff);
+            return;
+        }
         constexpr int64_t S = elem_bytes(K);
         const char* tb = (const char*)p + t0 * S;  // wave-uniform
         const uint32_t bytes = (uint32_t)((t1 - t0) * S);
@@ -175,7 +181,7 @@ __device__ __forceinline__ void loadn_tile(const void* p, int64_t t0, int64_t t1
         const uint32_t hi = (uint32_t)((((uintptr_t)tb + bytes) & ~(uintptr_t)127) - (uintptr_t)tb);
         const uint32_t off = (uint32_t)((i0 - t0) * S);
         u32x4 w;
-        if (off < lo || off + (uint32_t)(N * S) > hi) w = load_words<K, N, 0>(r, off);
+        if ((head && off < lo) || (tail && off + (uint32_t)(N * S) > hi)) w = load_words<K, N, 0>(r, off);
         else w = load_words<K, N, kLoadNt>(r, off);
         words_to_f32<K, N>(w, x, estep, eoff);
     } else {
@@ -271,9 +277,9 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
     float h[U][kCqVec];
     float e[U][kCqVec];
     const float eoff = -128.0f * p.err_step;  // the 8-bit error's decoder offset
-    // Not with an 8-bit error: that kernel is bound by instruction issue, and the edge
-    // lanes' extra instructions cost it more than the shared lines do (0.620 against 0.611
-    // ms back to back on the 7B shard).
+    // Not with an 8-bit error: that kernel is bound by instruction issue, and with edge
+    // lanes it ran 1% slower back to back on the 7B shard (0.617 against 0.611 ms), though
+    // 1.5% faster cache-flushed (0.600 against 0.609).
     constexpr bool EDGE = kEdgeCached && EK != kI8;
 
     // Issue every load of the tile first.
@@ -282,15 +288,18 @@ __device__ __forceinline__ void cq_tile(const CqSegDev& sg, int64_t base, int la
         float g[kCqVec];
         if constexpr (FULL && !SPLIT) {
             const int64_t i0 = base + u * SUB + LY::piece(lane, 0);
-            loadn_tile<GK, 8, true, EDGE>(sg.g, base, base + U * SUB, i0, g, 0.0f, 0.0f);
-            loadn_tile<EK, 8, ENT, EDGE>(sg.e, base, base + U * SUB, i0, e[u], p.err_step, eoff);
+            const bool head = u == 0, tail = u == U - 1;  // rows: the sub-tiles
+            loadn_tile<GK, 8, true, EDGE>(sg.g, base, base + U * SUB, i0, head, tail, g, 0.0f, 0.0f);
+            loadn_tile<EK, 8, ENT, EDGE>(sg.e, base, base + U * SUB, i0, head, tail, e[u], p.err_step, eoff);
         } else {
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 const int64_t i0 = base + u * SUB + LY::piece(lane, pc);
                 if constexpr (FULL) {
-                    loadn_tile<GK, 4, true, EDGE>(sg.g, base, base + U * SUB, i0, g + 4 * pc, 0.0f, 0.0f);
-                    loadn_tile<EK, 4, ENT, EDGE>(sg.e, base, base + U * SUB, i0, e[u] + 4 * pc, p.err_step, eoff);
+                    const bool head = u == 0 && pc == 0, tail = u == U - 1 && pc == 1;  // rows: the pieces
+                    loadn_tile<GK, 4, true, EDGE>(sg.g, base, base + U * SUB, i0, head, tail, g + 4 * pc, 0.0f, 0.0f);
+                    loadn_tile<EK, 4, ENT, EDGE>(sg.e, base, base + U * SUB, i0, head, tail, e[u] + 4 * pc,
+                                                 p.err_step, eoff);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
