@@ -206,6 +206,61 @@ def test_cq_deterministic_and_stream(gpu_lib):
 
 # -- the paper's 8-bit error and its periodic reset (LoCo Sec. 3.2, Eqn. (7)) ---------------
 
+ES = {"f32": 4, "bf16": 2, "i8": 1}
+
+
+@pytest.mark.parametrize("gd,ed", [("bf16", "f32"), ("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"),
+                                   ("bf16", "i8")])
+@pytest.mark.parametrize("block", [64, 256])
+def test_cq_segments_inside_lines(gpu_lib, gd, ed, block):
+    """Segments that are views into one flat gradient and one flat error, as an FSDP
+    rank's partitions are, starting at every 16-byte-aligned offset within a 128-byte line
+    that the element sizes allow.  A wave tile's first and last line of a stream then also
+    hold a neighbouring tile's elements, and the kernel loads the lanes in those lines
+    with another cache policy; the results must be the oracle's all the same (3-step
+    chain, 4-bit, several tiles per segment)."""
+    g16 = max(16 // ES[gd], 16 // ES[ed])  # elements per 16 bytes of the sparser stream
+    sizes = [g16 * (597 + k) for k in range(16)]
+    starts = np.concatenate([[0], np.cumsum(sizes)[:-1]]).tolist()
+    total = sum(sizes)
+    say(f"cq segments inside lines: {gd}/{ed} B={block}, 16 segments of {sizes[0]}..{sizes[-1]}")
+    gflat = torch.empty(total, dtype=TD[gd], device="cuda")
+    eflat = torch.zeros(total, dtype=TD[ed], device="cuda")
+    # every start offset within a line that 16-byte alignment allows is present
+    for flat, es in ((gflat, ES[gd]), (eflat, ES[ed])):
+        got = {(flat.data_ptr() + o * es) % 128 for o in starts}
+        assert got == set(range(0, 128, g16 * es)), (got, es)
+    codes = [Guarded(gpu_lib.code_bytes(n, 4), torch.uint8) for n in sizes]
+    absmax = [Guarded(gpu_lib.num_blocks(n, block), torch.float32) for n in sizes]
+    e_ora = [np.zeros(n, ORA_E[ed]) for n in sizes]
+    s_e = 2.0 ** 17 if ed == "i8" else 0.0
+    bitwise = True
+    for step in range(3):
+        gall = grads(step, total, gd, f"inline-{gd}-{ed}-{block}")
+        gflat.copy_(gall.to("cuda"))
+        segs = [(gflat[o:o + n], eflat[o:o + n], c.t, a.t) for o, n, c, a in zip(starts, sizes, codes, absmax)]
+        gpu_lib.loco_compensate_quantize_ex(segs, bits=4, block=block, beta=0.9, err_scale=s_e)
+        torch.cuda.synchronize()
+        for i, (o, n) in enumerate(zip(starts, sizes)):
+            ref = oracle.compensate_quantize(storage(gall[o:o + n], gd), e_ora[i], bits=4, block=block, beta=0.9,
+                                             grad_dtype=gd, err_dtype=ed, err_scale=s_e)
+            tag = f"step {step} segment {i} (start {o}, n={n})"
+            assert_bytes_equal(host(codes[i].t), ref["codes"], f"{tag} codes")
+            assert_bytes_equal(host(absmax[i].t).view(np.uint32), ref["absmax"].view(np.uint32), f"{tag} absmax")
+            e_seg = eflat[o:o + n]
+            if ed == "i8":
+                assert_bytes_equal(host(e_seg), ref["e_new"], f"{tag} 8-bit error")
+            elif ed == "f32":
+                bitwise &= assert_f32_close(host(e_seg), ref["e_new"], step_per_elem(ref["absmax"], 4, block, n),
+                                            f"{tag} error")
+            else:
+                bitwise &= assert_bf16_close(bf16_bits(e_seg), ref["e_new"], f"{tag} error")
+            e_ora[i] = ref["e_new"]
+            codes[i].check(f"{tag} codes")
+            absmax[i].check(f"{tag} absmax")
+    say("  error buffer bitwise equal:", bitwise)
+
+
 @pytest.mark.parametrize("s_e", [2.0 ** 18, 300_000.0])
 def test_cq_i8_error_tiny(gpu_lib, s_e):
     """The tiny workload with the error in 8 bits (s_e a power of two, and not), reset
