@@ -198,7 +198,7 @@ __device__ __forceinline__ void store4f(float* dst, int64_t i0, const float* x) 
 }
 
 // The fused Adam step holds the optimizer state of its sub-tile in registers besides the
-// payload codes: 84 VGPRs, 5 waves per SIMD (capped at 6 it spills).
+// payload codes: 87 VGPRs, 5 waves per SIMD (capped at 6 it spills).
 #ifndef LOCO_DRA_WAVES_PER_EU
 #define LOCO_DRA_WAVES_PER_EU 5
 #endif
