@@ -56,7 +56,8 @@ KERNEL_FILES = {"compensate_quantize_4bit": ["cq.hip"], "dequant_reduce_8peers":
                 "compensate_quantize_8bit_7b_shard": ["cq.hip"], "compensate_quantize_4bit_i8err_7b_shard": ["cq.hip"],
                 "compensate_quantize_4bit_llama_layer": ["cq.hip"], "compensate_quantize_4bit_moe": ["cq.hip"],
                 "dequant_reduce_adam_8peers": ["dr.hip"],
-                "sparseloco_topk_2bit": ["tk.hip"], "sparseloco_aggregate_8peers": ["sa.hip"]}
+                "sparseloco_topk_2bit": ["tk.hip"], "sparseloco_aggregate_8peers": ["sa.hip"],
+                "sparseloco_aggregate_8peers_bf16": ["sa.hip"]}
 COMMON_FILES = ["loco_device.hpp", "loco_internal.hpp"]
 
 
@@ -540,7 +541,23 @@ def main():
                      lambda sps=sps: oracle_module().sparse_aggregate(sps, sch * TK_CHUNK, chunk=TK_CHUNK, k=TK_K,
                                                                      bits=2, out_scale=1.0 / PARTS),
                      sa_bytes(sch * TK_CHUNK, PARTS, TK_CHUNK, TK_K, 2, 4), f"the first {sch:,} chunks of the 8 payloads"))
-        del spays, sout
+        del sout
+        # the same aggregation into bf16, which takes the library's other kernel (the
+        # persistent streaming one, with its read passes); no traffic twin has its shape
+        sob = torch.empty(nt, dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda: loco.loco_sparse_aggregate(spays, nt, chunk=TK_CHUNK, k=TK_K, bits=2, out=sob,
+                                                      out_scale=1.0 / PARTS, stream=stream),
+                   stream, reps)
+        bsb = sa_bytes(nt, PARTS, TK_CHUNK, TK_K, 2, 2)
+        modes["sparseloco_aggregate_8peers_bf16"] = {
+            "workload": f"8 peers' Top-k payloads of {nt:,} (chunk 4096, k=82, 2-bit) into bf16 x 1/8",
+            "avg_ms": round(ms, 4), **spread(), "alg_bytes": bsb, "GBps": round(bsb / ms / 1e6, 1),
+            "frac_hbm": round(bsb / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        jobs.append(("sparseloco_aggregate_8peers_bf16",
+                     lambda sps=sps: oracle_module().sparse_aggregate(sps, sch * TK_CHUNK, chunk=TK_CHUNK, k=TK_K,
+                                                                     bits=2, out_scale=1.0 / PARTS, out_dtype="bf16"),
+                     sa_bytes(sch * TK_CHUNK, PARTS, TK_CHUNK, TK_K, 2, 2), f"the first {sch:,} chunks of the 8 payloads"))
+        del spays, sob
 
         # the tiny case: 1,048,576 fp32 elements, one compensate-quantize (4-bit, block 128)
         # and the dequant-reduce of 4 peers into fp32 x 1/4 per step.  Its 19.6 MB sit in the

@@ -65,6 +65,7 @@ def test_sparseloco_bytes():
     assert oracle.tk_algorithmic_bytes(n, C, k, 2) == 3_233_611_776
     # sparse aggregation: 8 peers' payloads read, fp32 out written
     assert bench.sa_bytes(n, 8, C, k, 2, 4) == 8 * chunks * (164 + 21 + 4) + 4 * n == 1_172_832_256
+    assert bench.sa_bytes(n, 8, C, k, 2, 2) == 8 * chunks * (164 + 21 + 4) + 2 * n == 635_961_344
     assert oracle.sa_algorithmic_bytes(n, 8, C, k, 2, 4) == 1_172_832_256
 
 
