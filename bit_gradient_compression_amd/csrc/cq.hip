@@ -155,15 +155,15 @@ __device__ __forceinline__ u32x4 load_words(__amdgpu_buffer_rsrc_t r, uint32_t o
 #endif
 constexpr bool kEdgeCached = LOCO_CQ_EDGE_CACHED != 0;
 
-// N elements of kind K at element i0 of a full wave tile [t0, t1) of stream p, as loadn
-// with policy NT, except (EDGE) for the lanes in a shared edge line.  The loads go through
-// a buffer resource over the tile, whose cache policy is an immediate: two global loads of
-// one address that differ only in policy would be merged into one.
 template <int K, int N, bool NT>
 __device__ __forceinline__ void loadn(const void* p, int64_t i0, float* x, float estep, float eoff);
 
-// head / tail: this load instruction's row holds the tile's first / last element (a
-// row in between has no shared edge line and loads as loadn does).
+// N elements of kind K at element i0 of a full wave tile [t0, t1) of stream p, as loadn
+// with policy NT, except (EDGE) for the lanes in a shared edge line.  head / tail: this
+// load instruction's row holds the tile's first / last element; a row in between has no
+// shared edge line and loads as loadn does.  The edge rows load through a buffer resource
+// over the tile, whose cache policy is an immediate: two global loads of one address that
+// differ only in policy would be merged into one.
 template <int K, int N, bool NT, bool EDGE>
 __device__ __forceinline__ void loadn_tile(const void* p, int64_t t0, int64_t t1, int64_t i0, bool head, bool tail,
                                            float* x, float estep, float eoff) {
